@@ -1,0 +1,134 @@
+/*
+ * moe_decode.h -- C ABI of the output-centric ("warp decode") MoE decode layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: Cursor, "warp decode" blog post.  The MoE FFN of one
+ * decode step is two kernels (section "What we changed"):
+ *   moe_decode_gate_up  -- section "How the two kernels work", first two
+ *       paragraphs: for each token b, routed slot j and intermediate neuron n,
+ *       the gate and up rows of expert e = topk_ids[b,j] are streamed, their
+ *       MXFP8 values converted to FP32 on the fly and dotted with x[b] in FP32;
+ *       the neuron's value SiLU(gate) * up is written once.
+ *   moe_decode_down     -- same section, third and fourth paragraphs: for each
+ *       token b and output dimension o, the down rows of the token's k routed
+ *       experts are streamed against h[b,j,:], each expert's router weight is
+ *       folded into one FP32 accumulator, and y[b,o] is written once; the
+ *       weighted top-k combine is part of the projection (no padding, no
+ *       expert-major gather, no per-expert output buffer, no separate combine:
+ *       sections "Stage elimination" and "Eliminating buffers").
+ *
+ * Number formats.  Weights are MXFP8 (OCP Microscaling v1.0): E4M3 element
+ * codes (bias 7, max 448, S.1111.111 = NaN) with one E8M0 scale code
+ * (value 2^(v-127), 0xFF = NaN) per 32 consecutive elements along the
+ * reduction dimension.  Activations x, the intermediate h and the output y
+ * are bf16 (stored as 16-bit patterns); results are rounded to nearest even.
+ * Accumulation is FP32 in an unspecified order.  Router weights are FP32 and
+ * are used as given (never renormalised).
+ *
+ * Layouts (all row-major, all contiguous):
+ *   x            bf16   [B, H]
+ *   topk_ids     int32  [B, k]   expert of slot j of token b
+ *   topk_weights fp32   [B, k]   router weight of that slot
+ *   w_gate, w_up uint8  [E, I, H]    E4M3 codes, row = one neuron of one expert
+ *   s_gate, s_up uint8  [E, I, H/32] E8M0 codes, s[e,n,c/32] scales w[e,n,c]
+ *   w_down       uint8  [E, H, I]    E4M3 codes, row = one output dim of one expert
+ *   s_down       uint8  [E, H, I/32] E8M0 codes
+ *   h            bf16   [B, k, I]    slot order = topk_ids order
+ *   y            bf16   [B, H]
+ *
+ * Ownership and behaviour common to every call:
+ *   - Every pointer is a device pointer owned by the caller.  The library
+ *     allocates nothing, keeps no pointer after return and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     null stream).  The call returns as soon as the launch is enqueued; the
+ *     caller synchronises the stream before reading outputs.
+ *   - Calls are thread-safe (the library has no mutable state).
+ *   - Outputs are fully overwritten; every element is written exactly once.
+ *   - Outputs must not overlap any input (checked on the host).
+ *   - B == 0 is a valid no-op.
+ *   - topk_ids outside [0, E) are not read through: every output that depends
+ *     on such a slot is written as a quiet NaN.  Duplicate ids in one token
+ *     are legal and are summed slot by slot.
+ *   - E8M0 codes 0x00 (2^-127) and 0xFF (NaN) are honoured.
+ * Return value: MOE_OK (0) once the launch is enqueued, else a negative code
+ * below.  On any negative return other than MOE_ERR_LAUNCH nothing was
+ * launched and no output was touched.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL (with B > 0)                    */
+#define MOE_ERR_SHAPE (-2)       /* B<0, H/I/E/k<=0, k>E, H or I not a multiple of 32, or a   */
+                                 /* shape beyond the supported range (H <= 8192, k*I <= 16384) */
+#define MOE_ERR_ALIGN (-3)       /* x, h, w_* not 16-byte aligned; ids/weights not 4-byte     */
+#define MOE_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for the launch          */
+#define MOE_ERR_ALIAS (-5)       /* an output range overlaps an input range                   */
+#define MOE_ERR_ARG (-6)         /* an invalid tuning argument (see the _ex variants)         */
+
+/* Gate/up kernel: h[b,j,n] = bf16( SiLU(G) * U ), with
+ *   G = sum_c dec(w_gate[e,n,c]) * 2^(s_gate[e,n,c/32]-127) * x[b,c],
+ *   U = the same with w_up, s_up,  e = topk_ids[b,j].
+ * Reads x [B,H], topk_ids [B,k], w_gate/s_gate/w_up/s_up of the routed experts only;
+ * writes h_out [B,k,I]. */
+int moe_decode_gate_up(const void *x, const int32_t *topk_ids,
+                       const uint8_t *w_gate, const uint8_t *s_gate,
+                       const uint8_t *w_up, const uint8_t *s_up,
+                       void *h_out,
+                       int B, int H, int I, int E, int k, void *stream);
+
+/* Down kernel: y[b,o] = bf16( sum_j topk_weights[b,j] *
+ *   sum_i dec(w_down[e_j,o,i]) * 2^(s_down[e_j,o,i/32]-127) * h[b,j,i] ),  e_j = topk_ids[b,j].
+ * Reads h [B,k,I], topk_ids and topk_weights [B,k], w_down/s_down of the routed experts only;
+ * writes y_out [B,H]. */
+int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_weights,
+                    const uint8_t *w_down, const uint8_t *s_down,
+                    void *y_out,
+                    int B, int H, int I, int E, int k, void *stream);
+
+/* Tuning variants of the two calls: the same contract and results within the
+ * same tolerance, with the launch shape given explicitly instead of taken
+ * from the built-in table.  rows_per_wave in {1, 2, 4, 8} is the number of
+ * neurons (gate/up) or output dimensions (down) one 64-lane wavefront owns;
+ * 0 selects the table's choice.  Other values return MOE_ERR_ARG. */
+int moe_decode_gate_up_ex(const void *x, const int32_t *topk_ids,
+                          const uint8_t *w_gate, const uint8_t *s_gate,
+                          const uint8_t *w_up, const uint8_t *s_up,
+                          void *h_out,
+                          int B, int H, int I, int E, int k,
+                          int rows_per_wave, void *stream);
+int moe_decode_down_ex(const void *h, const int32_t *topk_ids, const float *topk_weights,
+                       const uint8_t *w_down, const uint8_t *s_down,
+                       void *y_out,
+                       int B, int H, int I, int E, int k,
+                       int rows_per_wave, void *stream);
+
+/* The launch shape the built-in table picks for a call (for reports):
+ * writes rows_per_wave and the number of workgroups; returns 0 or a negative code. */
+int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int *rows_per_wave, int *workgroups);
+int moe_decode_down_plan(int B, int H, int I, int E, int k, int *rows_per_wave, int *workgroups);
+
+/* Bandwidth probes that set the denominator of the efficiency figure (blog
+ * post, "Hardware efficiency": peak measured with a copy kernel over
+ * contiguous memory).  copy: dst[0:bytes) = src[0:bytes); read: reads
+ * src[0:bytes) and writes nothing unless an impossible checksum appears
+ * (sink: one 4-byte device word).  bytes must be a positive multiple of 16,
+ * pointers 16-byte aligned, src and dst disjoint.  Asynchronous on `stream`. */
+int moe_decode_copy_peak(const void *src, void *dst, size_t bytes, void *stream);
+int moe_decode_read_peak(const void *src, size_t bytes, void *sink, void *stream);
+
+/* Static description of a return code (never NULL). */
+const char *moe_decode_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,277 @@
+// C ABI of the warp-decode MoE layer for gfx950: argument validation, launch
+// shape selection and kernel launches.  The contract of every entry point is
+// stated in include/moe_decode.h.
+#include <hip/hip_runtime.h>
+
+#include "moe_decode.h"
+#include "down.hpp"
+#include "gate_up.hpp"
+#include "peak.hpp"
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;   // 256 threads = 4 independent 64-lane wavefronts
+constexpr int kMaxGateUpNbl = 4;    // H <= 4 * 64 * 32 = 8192
+constexpr int kMaxDownNbl = 8;      // k * I <= 8 * 64 * 32 = 16384
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int check_shape(int B, int H, int I, int E, int k) {
+  if (B < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_SHAPE;
+  if (H % 32 || I % 32) return MOE_ERR_SHAPE;
+  if (H > kMaxGateUpNbl * 64 * 32) return MOE_ERR_SHAPE;
+  if ((long long)k * I > (long long)kMaxDownNbl * 64 * 32) return MOE_ERR_SHAPE;
+  // wave ids and slot indices are 32-bit
+  if ((long long)B * k * I >= (1LL << 31) || (long long)B * H >= (1LL << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int blocks_per_lane(int blocks) { return (blocks + 63) / 64; }
+
+// ---------------------------------------------------------------- gate/up
+bool gate_up_allowed(int nbl, int r) { return (r == 1 || r == 2 || r == 4 || r == 8) && nbl * r <= 8; }
+
+int gate_up_default_rows(int B, int H, int I, int k) {
+  const int nbl = blocks_per_lane(H / 32);
+  const long long slots = (long long)B * k;
+  int r = 4;
+  while (r > 1 && (!gate_up_allowed(nbl, r) || slots * ((I + r - 1) / r) < 8192)) r /= 2;
+  return r;
+}
+
+template <int NBL, int R>
+void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
+                      const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
+  hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NBL, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
+                     tiles);
+}
+
+using GateUpLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
+                              const uint8_t*, const uint8_t*, void*, int, int, int, int, int, int);
+
+template <int NBL, int R>
+GateUpLaunch gate_up_fn() {
+  if constexpr (NBL * R <= 8) return launch_gate_up_t<NBL, R>;
+  else return nullptr;
+}
+
+template <int NBL>
+GateUpLaunch pick_gate_up_r(int r) {
+  switch (r) {
+    case 1: return gate_up_fn<NBL, 1>();
+    case 2: return gate_up_fn<NBL, 2>();
+    case 4: return gate_up_fn<NBL, 4>();
+    case 8: return gate_up_fn<NBL, 8>();
+  }
+  return nullptr;
+}
+
+GateUpLaunch pick_gate_up(int nbl, int r) {
+  switch (nbl) {
+    case 1: return pick_gate_up_r<1>(r);
+    case 2: return pick_gate_up_r<2>(r);
+    case 3: return pick_gate_up_r<3>(r);
+    case 4: return pick_gate_up_r<4>(r);
+  }
+  return nullptr;
+}
+
+int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg, const uint8_t* wu,
+                 const uint8_t* su, void* h, int B, int H, int I, int E, int k, int rows, void* stream) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if (B == 0) return MOE_OK;
+  if (!x || !ids || !wg || !sg || !wu || !su || !h) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(h, 16) || !aligned(ids, 4))
+    return MOE_ERR_ALIGN;
+  const size_t hb = (size_t)B * k * I * 2, wb = (size_t)E * I * H, sb = wb / 32;
+  if (overlaps(h, hb, x, (size_t)B * H * 2) || overlaps(h, hb, ids, (size_t)B * k * 4) || overlaps(h, hb, wg, wb) ||
+      overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
+    return MOE_ERR_ALIAS;
+  const int nbl = blocks_per_lane(H / 32);
+  if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
+  if (!gate_up_allowed(nbl, rows)) return MOE_ERR_ARG;
+  GateUpLaunch fn = pick_gate_up(nbl, rows);
+  if (!fn) return MOE_ERR_ARG;
+  const int tiles = (I + rows - 1) / rows;
+  const long long waves = (long long)tiles * B * k;
+  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+  (void)hipGetLastError();
+  fn(grid, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------- down
+bool down_allowed(int nbl, int r) {
+  return (r == 1 || r == 2 || r == 4 || r == 8) && nbl >= 1 && nbl <= kMaxDownNbl && nbl * (8 * r + 16) <= 192;
+}
+
+int down_default_rows(int B, int H, int I, int k) {
+  const int nbl = blocks_per_lane(k * I / 32);
+  int r = 4;
+  while (r > 1 && (!down_allowed(nbl, r) || (long long)B * ((H + r - 1) / r) < 8192)) r /= 2;
+  return r;
+}
+
+template <int NBL, int R>
+void launch_down_t(dim3 grid, hipStream_t st, const void* h, const int32_t* ids, const float* tw, const uint8_t* wd,
+                   const uint8_t* sd, void* y, int B, int H, int I, int E, int k, int tiles) {
+  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NBL, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+                     static_cast<const uint16_t*>(h), ids, tw, wd, sd, static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
+}
+
+using DownLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const float*, const uint8_t*,
+                            const uint8_t*, void*, int, int, int, int, int, int);
+
+template <int NBL, int R>
+DownLaunch down_fn() {
+  if constexpr (NBL * (8 * R + 16) <= 192) return launch_down_t<NBL, R>;
+  else return nullptr;
+}
+
+template <int NBL>
+DownLaunch pick_down_r(int r) {
+  switch (r) {
+    case 1: return down_fn<NBL, 1>();
+    case 2: return down_fn<NBL, 2>();
+    case 4: return down_fn<NBL, 4>();
+    case 8: return down_fn<NBL, 8>();
+  }
+  return nullptr;
+}
+
+DownLaunch pick_down(int nbl, int r) {
+  switch (nbl) {
+    case 1: return pick_down_r<1>(r);
+    case 2: return pick_down_r<2>(r);
+    case 3: return pick_down_r<3>(r);
+    case 4: return pick_down_r<4>(r);
+    case 5: return pick_down_r<5>(r);
+    case 6: return pick_down_r<6>(r);
+    case 7: return pick_down_r<7>(r);
+    case 8: return pick_down_r<8>(r);
+  }
+  return nullptr;
+}
+
+int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t* wd, const uint8_t* sd, void* y,
+              int B, int H, int I, int E, int k, int rows, void* stream) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if (B == 0) return MOE_OK;
+  if (!h || !ids || !tw || !wd || !sd || !y) return MOE_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(wd, 16) || !aligned(y, 2) || !aligned(ids, 4) || !aligned(tw, 4))
+    return MOE_ERR_ALIGN;
+  const size_t yb = (size_t)B * H * 2, wb = (size_t)E * H * I;
+  if (overlaps(y, yb, h, (size_t)B * k * I * 2) || overlaps(y, yb, ids, (size_t)B * k * 4) ||
+      overlaps(y, yb, tw, (size_t)B * k * 4) || overlaps(y, yb, wd, wb) || overlaps(y, yb, sd, wb / 32))
+    return MOE_ERR_ALIAS;
+  const int nbl = blocks_per_lane(k * I / 32);
+  if (rows == 0) rows = down_default_rows(B, H, I, k);
+  if (!down_allowed(nbl, rows)) return MOE_ERR_ARG;
+  DownLaunch fn = pick_down(nbl, rows);
+  if (!fn) return MOE_ERR_ARG;
+  const int tiles = (H + rows - 1) / rows;
+  const long long waves = (long long)tiles * B;
+  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+  (void)hipGetLastError();
+  fn(grid, static_cast<hipStream_t>(stream), h, ids, tw, wd, sd, y, B, H, I, E, k, tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* w_gate, const uint8_t* s_gate,
+                       const uint8_t* w_up, const uint8_t* s_up, void* h_out, int B, int H, int I, int E, int k,
+                       void* stream) {
+  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, 0, stream);
+}
+
+int moe_decode_gate_up_ex(const void* x, const int32_t* topk_ids, const uint8_t* w_gate, const uint8_t* s_gate,
+                          const uint8_t* w_up, const uint8_t* s_up, void* h_out, int B, int H, int I, int E, int k,
+                          int rows_per_wave, void* stream) {
+  if (rows_per_wave < 0) return MOE_ERR_ARG;
+  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, rows_per_wave, stream);
+}
+
+int moe_decode_down(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
+                    const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, void* stream) {
+  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, 0, stream);
+}
+
+int moe_decode_down_ex(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
+                       const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, int rows_per_wave,
+                       void* stream) {
+  if (rows_per_wave < 0) return MOE_ERR_ARG;
+  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, rows_per_wave, stream);
+}
+
+int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* rows_per_wave, int* workgroups) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if (!rows_per_wave || !workgroups) return MOE_ERR_NULL;
+  const int r = gate_up_default_rows(B, H, I, k);
+  *rows_per_wave = r;
+  *workgroups = (int)((((long long)(I + r - 1) / r) * B * k + kWavesPerBlock - 1) / kWavesPerBlock);
+  return MOE_OK;
+}
+
+int moe_decode_down_plan(int B, int H, int I, int E, int k, int* rows_per_wave, int* workgroups) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if (!rows_per_wave || !workgroups) return MOE_ERR_NULL;
+  const int r = down_default_rows(B, H, I, k);
+  *rows_per_wave = r;
+  *workgroups = (int)((((long long)(H + r - 1) / r) * B + kWavesPerBlock - 1) / kWavesPerBlock);
+  return MOE_OK;
+}
+
+int moe_decode_copy_peak(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return MOE_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_ALIGN;
+  if (overlaps(src, bytes, dst, bytes)) return MOE_ERR_ALIAS;
+  const size_t n = bytes / 16;
+  const size_t want = (n + 256 * 4 - 1) / (256 * 4);
+  const dim3 grid((unsigned)(want < 4096 ? want : 4096));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(moe::copy_peak_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const moe::u32x4*>(src), static_cast<moe::u32x4*>(dst), n);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int moe_decode_read_peak(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return MOE_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return MOE_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
+  const size_t n = bytes / 16;
+  const size_t want = (n + 256 * 4 - 1) / (256 * 4);
+  const dim3 grid((unsigned)(want < 4096 ? want : 4096));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(moe::read_peak_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const moe::u32x4*>(src), n, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+const char* moe_decode_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "unsupported or invalid shape";
+    case MOE_ERR_ALIGN: return "misaligned pointer (x, h, weights need 16 bytes; ids and router weights 4)";
+    case MOE_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    case MOE_ERR_ALIAS: return "an output overlaps an input";
+    case MOE_ERR_ARG: return "invalid tuning argument";
+  }
+  return "unknown error code";
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device primitives for the gfx950 (CDNA4) warp-decode kernels.
+//
+// - MXFP8 decode: E4M3 pairs become bf16 pairs with gfx950's
+//   v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value); the
+//   E8M0 block scale, a power of two, multiplies the block's FP32 partial sum
+//   once, which is exact barring overflow/underflow.
+// - Dot products: v_dot2c_f32_bf16 multiplies two bf16 pairs and accumulates
+//   in FP32, so one instruction does two multiply-adds on raw bf16 activations
+//   with no bf16->FP32 unpacking.
+// - Cross-lane sums use DPP row operations inside each 16-lane row and the
+//   gfx950 permlane16/permlane32 swaps across rows: no LDS traffic, no barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct alignas(16) u32x4 {
+  uint32_t v[4];
+};
+
+// 16-byte global load.
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u t = *reinterpret_cast<const v4u*>(p);
+  u32x4 r;
+  r.v[0] = t[0]; r.v[1] = t[1]; r.v[2] = t[2]; r.v[3] = t[3];
+  return r;
+}
+
+// E4M3 bytes 0,1 (hi=false) or 2,3 (hi=true) of `word` -> bf16 pair (exact).
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t word, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+// acc + a.x*b.x + a.y*b.y, FP32 accumulate.
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
+// E8M0 code -> FP32 value 2^(s-127); 0 -> 2^-127 (FP32 subnormal), 0xFF -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  uint32_t bits = s << 23;
+  bits = (s == 0u) ? 0x00400000u : bits;
+  bits = (s == 255u) ? 0x7FC00000u : bits;
+  return __builtin_bit_cast(float, bits);
+}
+
+// Dot product of one 32-element MXFP8 block (w: 2 x 16 bytes of E4M3) with 32
+// bf16 activations (xa: 4 x 16 bytes), returned unscaled in FP32.
+__device__ __forceinline__ float block_dot(const u32x4& w0, const u32x4& w1, const u32x4* xa, float acc) {
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const uint32_t word = (d < 4) ? w0.v[d] : w1.v[d - 4];
+    // elements 4d..4d+3 of the block; activations are dwords 2d and 2d+1
+    const uint32_t x01 = xa[(2 * d) >> 2].v[(2 * d) & 3];
+    const uint32_t x23 = xa[(2 * d + 1) >> 2].v[(2 * d + 1) & 3];
+    acc = dot2(e4m3x2_to_bf16x2(word, false), as_bf16x2(x01), acc);
+    acc = dot2(e4m3x2_to_bf16x2(word, true), as_bf16x2(x23), acc);
+  }
+  return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the row sum.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp<0x141>(v);   // row_half_mirror: quads 0<->1, 2<->3 of each 8-lane half
+  v += dpp<0x140>(v);   // row_mirror: halves of the 16-lane row
+  return v;
+}
+
+// Sum over all 64 lanes; every lane gets the sum.
+__device__ __forceinline__ float wave_sum64(float v) {
+  v = row_sum16(v);
+  {
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);   // rows 0+1, 2+3
+  }
+  {
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);   // halves
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float silu(float g) {
+  return g / (1.0f + __expf(-g));
+}
+
+__device__ __forceinline__ float qnan() { return __builtin_bit_cast(float, 0x7FC00000u); }
+
+}  // namespace moe

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches the GPU).
+
+The library loads, exports every function include/moe_decode.h declares, and
+rejects bad arguments with the documented codes before any launch.  The
+pointers passed are plain integers: every case returns during host-side
+validation, which runs before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_gate_up_amd as mg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_decode_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(mg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mg.EXPORTS)
+
+
+def test_error_codes_match_header():
+    src = open(HEADER).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MOE_\w+) \(?(-?\d+)\)?", src)}
+    for name, val in codes.items():
+        assert getattr(mg, name) == val, name
+    for val in codes.values():
+        s = mg.strerror(val)
+        assert s and s != "unknown error code"
+    assert mg.strerror(12345) == "unknown error code"
+
+
+A = 0x100000000000   # 16-byte aligned fake device addresses, never dereferenced,
+S = 0x1000000000     # spaced 64 GiB apart so only the planted overlaps overlap
+
+
+def gu(x=A, ids=A + 1 * S, wg=A + 2 * S, sg=A + 3 * S, wu=A + 4 * S, su=A + 5 * S, h=A + 6 * S,
+       B=2, H=2048, I=768, E=128, k=8, rows=None):
+    L = mg.lib()
+    args = [ctypes.c_void_p(p) for p in (x, ids, wg, sg, wu, su, h)] + [B, H, I, E, k]
+    if rows is None:
+        return L.moe_decode_gate_up(*args, None)
+    return L.moe_decode_gate_up_ex(*args, rows, None)
+
+
+def dn(h=A, ids=A + 1 * S, tw=A + 2 * S, wd=A + 3 * S, sd=A + 4 * S, y=A + 5 * S,
+       B=2, H=2048, I=768, E=128, k=8, rows=None):
+    L = mg.lib()
+    args = [ctypes.c_void_p(p) for p in (h, ids, tw, wd, sd, y)] + [B, H, I, E, k]
+    if rows is None:
+        return L.moe_decode_down(*args, None)
+    return L.moe_decode_down_ex(*args, rows, None)
+
+
+@pytest.mark.parametrize("fn", [gu, dn])
+def test_shape_errors(fn):
+    assert fn(B=-1) == mg.MOE_ERR_SHAPE
+    assert fn(H=2047) == mg.MOE_ERR_SHAPE
+    assert fn(I=100) == mg.MOE_ERR_SHAPE
+    assert fn(k=0) == mg.MOE_ERR_SHAPE
+    assert fn(k=129) == mg.MOE_ERR_SHAPE
+    assert fn(E=0, k=1) == mg.MOE_ERR_SHAPE
+    assert fn(H=8192 + 32) == mg.MOE_ERR_SHAPE       # beyond 4 blocks per lane
+    assert fn(I=2048 + 32, k=8) == mg.MOE_ERR_SHAPE  # k*I beyond 8 blocks per lane
+
+
+def test_empty_batch_is_a_noop():
+    assert gu(B=0) == mg.MOE_OK
+    assert dn(B=0) == mg.MOE_OK
+    assert gu(B=0, x=0, h=0) == mg.MOE_OK            # no pointer is needed when B == 0
+
+
+def test_null_pointer_errors():
+    for name in ("x", "ids", "wg", "sg", "wu", "su", "h"):
+        assert gu(**{name: 0}) == mg.MOE_ERR_NULL, name
+    for name in ("h", "ids", "tw", "wd", "sd", "y"):
+        assert dn(**{name: 0}) == mg.MOE_ERR_NULL, name
+
+
+def test_alignment_errors():
+    for name in ("x", "wg", "wu", "h"):
+        assert gu(**{name: A + 8 * S + 8}) == mg.MOE_ERR_ALIGN, name
+    assert gu(ids=A + 8 * S + 2) == mg.MOE_ERR_ALIGN
+    for name in ("h", "wd"):
+        assert dn(**{name: A + 8 * S + 8}) == mg.MOE_ERR_ALIGN, name
+    assert dn(y=A + 8 * S + 1) == mg.MOE_ERR_ALIGN
+    assert dn(tw=A + 8 * S + 2) == mg.MOE_ERR_ALIGN
+
+
+def test_alias_errors():
+    # h_out overlapping x / the gate weights
+    assert gu(h=A + 16) == mg.MOE_ERR_ALIAS
+    assert gu(wg=A + 6 * S - 4096) == mg.MOE_ERR_ALIAS
+    # y overlapping h
+    assert dn(y=A + 64) == mg.MOE_ERR_ALIAS
+
+
+def test_bad_tuning_arguments():
+    assert gu(rows=3) == mg.MOE_ERR_ARG
+    assert gu(rows=-1) == mg.MOE_ERR_ARG
+    assert gu(rows=16) == mg.MOE_ERR_ARG
+    assert gu(H=8192, rows=4) == mg.MOE_ERR_ARG      # 4 blocks/lane x 4 rows exceeds the register budget
+    assert dn(rows=5) == mg.MOE_ERR_ARG
+    assert dn(I=1536, rows=8) == mg.MOE_ERR_ARG      # 6 blocks/lane x 8 rows exceeds the register budget
+
+
+def test_plans():
+    r, g = mg.moe_decode_gate_up_plan(32, 2048, 768, 128, 8)
+    assert r in (1, 2, 4, 8) and g == -(-((768 + r - 1) // r) * 32 * 8 // 4)
+    r, g = mg.moe_decode_down_plan(32, 2048, 768, 128, 8)
+    assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * 32 // 4)
+    with pytest.raises(mg.MoeDecodeError):
+        mg.moe_decode_gate_up_plan(1, 100, 768, 128, 8)
+
+
+def test_peak_argument_errors():
+    L = mg.lib()
+    v = ctypes.c_void_p
+    assert L.moe_decode_copy_peak(v(A), v(A + 1 * S), 0, None) == mg.MOE_ERR_SHAPE
+    assert L.moe_decode_copy_peak(v(A), v(A + 1 * S), 24, None) == mg.MOE_ERR_SHAPE
+    assert L.moe_decode_copy_peak(v(A + 8), v(A + 1 * S), 32, None) == mg.MOE_ERR_ALIGN
+    assert L.moe_decode_copy_peak(v(A), v(A + 16), 64, None) == mg.MOE_ERR_ALIAS
+    assert L.moe_decode_copy_peak(None, v(A), 64, None) == mg.MOE_ERR_NULL
+    assert L.moe_decode_read_peak(v(A), 0, v(A + 64), None) == mg.MOE_ERR_SHAPE
+    assert L.moe_decode_read_peak(v(A), 64, None, None) == mg.MOE_ERR_NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 2048), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mg.moe_decode_gate_up(x, torch.zeros((1, 8), dtype=torch.int32), *(torch.zeros(1, dtype=torch.uint8),) * 4,
+                              torch.zeros((1, 8, 768), dtype=torch.bfloat16), E=128, I=768)
