@@ -93,12 +93,15 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum64(acc[r]);
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum_row3(acc[r]);
 
+  // lanes 48..63 hold the sums; lane 48 + r writes output o0 + r
+  const int r_out = lane - kSumLane;
   float v = acc[0];
 #pragma unroll
-  for (int r = 1; r < R; ++r) v = (lane == r) ? acc[r] : v;
-  if (lane < R && o0 + lane < H) y[(size_t)b * H + o0 + lane] = f32_to_bf16_rne(bad_token ? qnan() : v);
+  for (int r = 1; r < R; ++r) v = (r_out == r) ? acc[r] : v;
+  if (r_out >= 0 && r_out < R && o0 + r_out < H)
+    y[(size_t)b * H + o0 + r_out] = f32_to_bf16_rne(bad_token ? qnan() : v);
 }
 
 }  // namespace moe

@@ -11,7 +11,7 @@
 // lane per block).  The lane's slice of x[b] is loaded once and reused for the
 // R gate rows and R up rows.  All 4*R*NBL weight loads are issued before any
 // arithmetic so each wave keeps R*4 KB in flight.  Per-lane partial sums are
-// reduced across the wave with DPP and permlane swaps, not LDS.
+// reduced across the wave with DPP row operations, not LDS.
 //
 // Grid order: wave id = tile * (B*k) + slot, tile (neuron group) slowest, so
 // all tokens that share an expert read that expert's rows close together in
@@ -95,20 +95,21 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    g[r] = wave_sum64(g[r]);
-    u[r] = wave_sum64(u[r]);
+    g[r] = wave_sum_row3(g[r]);
+    u[r] = wave_sum_row3(u[r]);
   }
 
-  // lane r < R writes neuron n0 + r
+  // lanes 48..63 hold the sums; lane 48 + r writes neuron n0 + r
+  const int r_out = lane - kSumLane;
   float gv = g[0], uv = u[0];
 #pragma unroll
   for (int r = 1; r < R; ++r) {
-    gv = (lane == r) ? g[r] : gv;
-    uv = (lane == r) ? u[r] : uv;
+    gv = (r_out == r) ? g[r] : gv;
+    uv = (r_out == r) ? u[r] : uv;
   }
-  if (lane < R && n0 + lane < I) {
+  if (r_out >= 0 && r_out < R && n0 + r_out < I) {
     const float hv = bad ? qnan() : silu(gv) * uv;
-    h[(size_t)s * I + n0 + lane] = f32_to_bf16_rne(hv);
+    h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(hv);
   }
 }
 

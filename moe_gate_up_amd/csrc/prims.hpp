@@ -7,8 +7,9 @@
 // - Dot products: v_dot2c_f32_bf16 multiplies two bf16 pairs and accumulates
 //   in FP32, so one instruction does two multiply-adds on raw bf16 activations
 //   with no bf16->FP32 unpacking.
-// - Cross-lane sums use DPP row operations inside each 16-lane row and the
-//   gfx950 permlane16/permlane32 swaps across rows: no LDS traffic, no barrier.
+// - Cross-lane sums use DPP: quad permutes and mirrors inside each 16-lane row,
+//   then the row broadcasts (row_bcast:15, row_bcast:31) across rows.  No LDS
+//   traffic, no barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,9 +68,10 @@ __device__ __forceinline__ float block_dot(const u32x4& w0, const u32x4& w1, con
   return acc;
 }
 
-template <int CTRL>
+// DPP move of v; lanes in rows outside ROW_MASK read 0 (the identity of +).
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
 // Sum over the 16 lanes of each DPP row; every lane of the row gets the row sum.
@@ -81,17 +83,14 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Sum over all 64 lanes; every lane gets the sum.
-__device__ __forceinline__ float wave_sum64(float v) {
+// Sum over all 64 lanes.  The total lands in every lane of row 3 (lanes 48..63);
+// other rows hold partial sums.  row_bcast:15 adds row 0's sum into row 1 and
+// row 2's into row 3; row_bcast:31 then adds lane 31 (rows 0+1) into row 3.
+constexpr int kSumLane = 48;
+__device__ __forceinline__ float wave_sum_row3(float v) {
   v = row_sum16(v);
-  {
-    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
-    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);   // rows 0+1, 2+3
-  }
-  {
-    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
-    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);   // halves
-  }
+  v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
   return v;
 }
 

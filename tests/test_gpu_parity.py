@@ -65,8 +65,9 @@ def check(h, y, h_ref, y_ref, B, k, what=""):
     print(f"{what} h: {ph}\n{what} y: {py}", flush=True)
     assert passes(ph), (what, ph)
     assert passes(py), (what, py)
-    # a handful of one-step differences at most (FP32 vs FP64 accumulation)
-    assert ph["n_diff"] <= max(8, ph["n"] // 200) and py["n_diff"] <= max(8, py["n"] // 200)
+    # FP32 accumulation flips the bf16 rounding of a few near-ties (and y inherits h's
+    # flips); a systematic rounding error (e.g. truncation) would flip about half
+    assert ph["n_diff"] <= max(8, ph["n"] // 20) and py["n_diff"] <= max(8, py["n"] // 20)
 
 
 # --------------------------------------------------------------- decode path
