@@ -20,6 +20,9 @@ Weights: one layer is generated on the host (seed 0) and uploaded into
 consecutive steps never read the same addresses and the 256 MB last-level
 cache (MALL) cannot serve a step from the previous one.
 
+The timed loops are captured into HIP graphs and replayed, as a decode server
+would run a step; the timed region starts after the inputs are resident.
+
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
 from __future__ import annotations
@@ -67,8 +70,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+    reads for a copy kernel of known size) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         d = json.load(open(p))
@@ -76,7 +80,8 @@ def measured_traffic(kernel: str):
         return None
     if d.get("source_hash") != kernel_source_hash():
         return None
-    return d.get("kernels", {}).get(kernel)
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes")
 
 
 def main():
@@ -169,54 +174,66 @@ def main():
             info.append(layer_bytes(ids, H, I, k))
         return (up(np.stack(xs)), up(np.stack(ids_l)), up(np.stack(ws)), info)
 
-    def run_steps(B, steps, warmup, n_rout, kernel_events=False):
+    def run_steps(B, steps, warmup, n_rout):
+        """Time `steps` whole-layer steps (both kernels), then each kernel alone in a
+        back-to-back loop of `steps` launches (same weight copies and routings).
+
+        Each loop is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
+        graph is replayed inside the timed region, so the figure is the GPU's time
+        for the launches and not the Python launch overhead, which at small B
+        exceeds the kernels' own duration.  One eager pass runs first."""
         xs, idss, wss, info = make_batch(B, n_rout, mi.routing_seed(2, B))
         h = torch.empty((B, k, I), dtype=torch.int16, device=dev)
         y = torch.empty((B, H), dtype=torch.int16, device=dev)
 
-        def step(i, ev=None):
-            wg, sg, wu, su, wd, sd = copies[i % len(copies)]
+        def gate_up(i):
+            wg, sg, wu, su, _, _ = copies[i % len(copies)]
             r = i % n_rout
-            if ev is not None:
-                ev[0].record(stream)
-            mg.moe_decode_gate_up(xs[r], idss[r], wg, sg, wu, su, h, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-            mg.moe_decode_down(h, idss[r], wss[r], wd, sd, y, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
+            mg.moe_decode_gate_up(xs[r], idss[r], wg, sg, wu, su, h)
 
-        for i in range(warmup):
-            step(i)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)] if kernel_events else None
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        start.record(stream)
-        for i in range(steps):
-            step(warmup + i, evs[i] if evs else None)
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        t = start.elapsed_time(end) / 1e3
-        byt = sum(info[(warmup + i) % n_rout]["total"] for i in range(steps))
-        res = dict(B=B, seconds=t, wall_seconds=wall, bytes=byt, us_per_layer=t / steps * 1e6,
-                   GBps=byt / t / 1e9, distinct_experts=float(np.mean([d["distinct"] for d in info])))
-        if evs:
-            gu = [e[0].elapsed_time(e[1]) / 1e3 for e in evs]
-            dn = [e[1].elapsed_time(e[2]) / 1e3 for e in evs]
-            gub = [info[(warmup + i) % n_rout]["gate_up"] for i in range(steps)]
-            dnb = [info[(warmup + i) % n_rout]["down"] for i in range(steps)]
-            res["gate_up_us"] = float(np.mean(gu)) * 1e6
-            res["down_us"] = float(np.mean(dn)) * 1e6
-            res["gate_up_GBps"] = float(np.mean(gub)) / float(np.mean(gu)) / 1e9
-            res["down_GBps"] = float(np.mean(dnb)) / float(np.mean(dn)) / 1e9
+        def down(i):
+            _, _, _, _, wd, sd = copies[i % len(copies)]
+            r = i % n_rout
+            mg.moe_decode_down(h, idss[r], wss[r], wd, sd, y)
+
+        def step(i):
+            gate_up(i)
+            down(i)
+
+        def timed(fn):
+            for i in range(warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(warmup + i)
+            g.replay()   # untimed first replay
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / 1e3, time.perf_counter() - w0
+
+        t, wall = timed(step)
         # sanity: outputs are finite (parity itself is checked by the test suite)
         assert torch.isfinite(y.view(torch.bfloat16).float()).all().item()
-        return res
+        t_gu, _ = timed(gate_up)
+        t_dn, _ = timed(down)
+        pick = [info[(warmup + i) % n_rout] for i in range(steps)]
+        byt = sum(d["total"] for d in pick)
+        gub = sum(d["gate_up"] for d in pick)
+        dnb = sum(d["down"] for d in pick)
+        return dict(B=B, seconds=t, wall_seconds=wall, bytes=byt, us_per_layer=t / steps * 1e6,
+                    GBps=byt / t / 1e9, distinct_experts=float(np.mean([d["distinct"] for d in info])),
+                    gate_up_us=t_gu / steps * 1e6, down_us=t_dn / steps * 1e6,
+                    gate_up_GBps=gub / t_gu / 1e9, down_GBps=dnb / t_dn / 1e9)
 
     B = args.batch
-    main_res = run_steps(B, args.steps, args.warmup, args.routings, kernel_events=True)
+    main_res = run_steps(B, args.steps, args.warmup, args.routings)
     kern = main_res
     log(f"B={B}: {main_res['us_per_layer']:.2f} us/layer, {main_res['GBps']:.0f} GB/s effective "
         f"({main_res['GBps'] / copy_gbps:.1%} of copy peak)")
@@ -225,7 +242,7 @@ def main():
 
     sweep = []
     for b in [int(s) for s in args.sweep.split(",") if s.strip()]:
-        r = run_steps(b, args.sweep_steps, 10, args.routings, kernel_events=True)
+        r = run_steps(b, args.sweep_steps, 10, args.routings)
         r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
         sweep.append({kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in r.items()
                       if kk not in ("seconds", "wall_seconds", "bytes")})

@@ -67,7 +67,8 @@ extern "C" {
 #define MOE_OK 0
 #define MOE_ERR_NULL (-1)        /* a required pointer is NULL (with B > 0)                    */
 #define MOE_ERR_SHAPE (-2)       /* B<0, H/I/E/k<=0, k>E, H or I not a multiple of 32, or a   */
-                                 /* shape beyond the supported range (H <= 8192, k*I <= 16384) */
+                                 /* shape beyond the supported range (H <= 8192,              */
+                                 /* k*I <= 16384, E*I*H < 2^32 bytes per weight tensor)       */
 #define MOE_ERR_ALIGN (-3)       /* x, h, w_* not 16-byte aligned; ids/weights not 4-byte     */
 #define MOE_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for the launch          */
 #define MOE_ERR_ALIAS (-5)       /* an output range overlaps an input range                   */

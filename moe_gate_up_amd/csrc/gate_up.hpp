@@ -9,13 +9,17 @@
 // each lane needs exactly one E8M0 scale byte per row and block, and the 64
 // lanes together cover 2048 contiguous bytes per row (two 16-byte loads per
 // lane per block).  The lane's slice of x[b] is loaded once and reused for the
-// R gate rows and R up rows.  All 4*R*NBL weight loads are issued before any
-// arithmetic so each wave keeps R*4 KB in flight.  Per-lane partial sums are
-// reduced across the wave with DPP row operations, not LDS.
+// R gate rows and R up rows.  The code is straight-line: every load of the
+// wave is issued before the first arithmetic, so each wave keeps R*4 KB in
+// flight; lanes past the end of a short row re-read the row's last block and
+// contribute zero.  Loads are buffer loads: scalar base, 32-bit lane offset,
+// scalar row offset.  Per-lane partial sums are reduced across the wave with DPP row
+// operations, not LDS.
 //
-// Grid order: wave id = tile * (B*k) + slot, tile (neuron group) slowest, so
-// all tokens that share an expert read that expert's rows close together in
-// time and the repeats are served from L2 / MALL instead of HBM.
+// Grid order: wave id = tile * (B*k) + slot, tile (neuron group) slowest, and
+// workgroups are remapped so that each XCD runs a contiguous range of tiles.
+// All tokens that share an expert then read that expert's rows at about the
+// same time on the same XCD, and the repeats hit that XCD's L2.
 #pragma once
 
 #include "prims.hpp"
@@ -29,53 +33,62 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     const uint8_t* __restrict__ wu, const uint8_t* __restrict__ su,
     uint16_t* __restrict__ h, int B, int H, int I, int E, int k, int n_tiles) {
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform: keep the index math in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
   const int slots = B * k;
   if (wave >= n_tiles * slots) return;
-  const int tile = wave / slots;
+  // integer division runs on the VALU; readfirstlane returns the (uniform) results to SGPRs
+  const int tile = __builtin_amdgcn_readfirstlane(wave / slots);
   const int s = wave - tile * slots;
-  const int b = s / k;
+  const int b = __builtin_amdgcn_readfirstlane(s / k);
   const int n0 = tile * R;
   const int nblk = H >> 5;
   const int e_raw = __builtin_amdgcn_readfirstlane(ids[s]);
   const bool bad = (unsigned)e_raw >= (unsigned)E;
   const int e = bad ? 0 : e_raw;
 
-  // x[b] slice: block q = lane + 64c covers elements [32q, 32q+32)
-  u32x4 xa[NBL][4];
+  // block of this lane in pass c, clamped to the row; `live` zeroes the clamped duplicates
+  uint32_t qb[NBL];
+  float live[NBL];
 #pragma unroll
   for (int c = 0; c < NBL; ++c) {
     const int q = lane + 64 * c;
-    if (q < nblk) {
-      const uint16_t* xp = x + (size_t)b * H + q * 32;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xa[c][t] = load16(xp + 8 * t);
-    }
+    qb[c] = (uint32_t)min(q, nblk - 1);
+    live[c] = q < nblk ? 1.0f : 0.0f;
   }
+
+  const uint32_t wbytes = (uint32_t)E * (uint32_t)I * (uint32_t)H;   // < 2^32, checked on the host
+  const rsrc_t xr = make_rsrc(x, (uint64_t)B * H * 2);
+  const rsrc_t gr = make_rsrc(wg, wbytes), ur = make_rsrc(wu, wbytes);
+  const rsrc_t gsr = make_rsrc(sg, wbytes / 32), usr = make_rsrc(su, wbytes / 32);
+
+  // x[b] slice: block q covers elements [32q, 32q+32) = bytes [64q, 64q+64)
+  const uint32_t xoff = (uint32_t)b * (uint32_t)H * 2u;
+  u32x4 xa[NBL][4];
+#pragma unroll
+  for (int c = 0; c < NBL; ++c)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xa[c][t] = bload16(xr, qb[c] * 64u + 16u * t, xoff);
 
   u32x4 gw[R][NBL][2], uw[R][NBL][2];
   uint32_t gsc[R][NBL], usc[R][NBL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = min(n0 + r, I - 1);   // clamp the ragged last tile; its result is not stored
-    const size_t row = (size_t)e * I + n;
-    const uint8_t* gp = wg + row * H;
-    const uint8_t* up = wu + row * H;
-    const uint8_t* gs = sg + row * nblk;
-    const uint8_t* us = su + row * nblk;
+    const uint32_t row = (uint32_t)(e * I + min(n0 + r, I - 1));   // ragged last tile: clamp, not stored
+    const uint32_t woff = row * (uint32_t)H, soff = row * (uint32_t)nblk;
 #pragma unroll
     for (int c = 0; c < NBL; ++c) {
-      const int q = lane + 64 * c;
-      if (q < nblk) {
-        gw[r][c][0] = load16(gp + q * 32);
-        gw[r][c][1] = load16(gp + q * 32 + 16);
-        uw[r][c][0] = load16(up + q * 32);
-        uw[r][c][1] = load16(up + q * 32 + 16);
-        gsc[r][c] = gs[q];
-        usc[r][c] = us[q];
-      }
+      gw[r][c][0] = bload16(gr, qb[c] * 32u, woff);
+      gw[r][c][1] = bload16(gr, qb[c] * 32u + 16u, woff);
+      uw[r][c][0] = bload16(ur, qb[c] * 32u, woff);
+      uw[r][c][1] = bload16(ur, qb[c] * 32u + 16u, woff);
+      gsc[r][c] = bload8(gsr, qb[c], soff);
+      usc[r][c] = bload8(usr, qb[c], soff);
     }
   }
+
+  // keep every load above this point: all of the wave's memory traffic is in flight at once
+  __builtin_amdgcn_sched_barrier(0);
 
   float g[R], u[R];
 #pragma unroll
@@ -84,13 +97,10 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     u[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < NBL; ++c) {
-      const int q = lane + 64 * c;
-      if (q < nblk) {
-        const float pg = block_dot(gw[r][c][0], gw[r][c][1], xa[c], 0.0f);
-        const float pu = block_dot(uw[r][c][0], uw[r][c][1], xa[c], 0.0f);
-        g[r] = fmaf(pg, e8m0_to_f32(gsc[r][c]), g[r]);
-        u[r] = fmaf(pu, e8m0_to_f32(usc[r][c]), u[r]);
-      }
+      const float pg = block_dot(gw[r][c][0], gw[r][c][1], xa[c], 0.0f);
+      const float pu = block_dot(uw[r][c][0], uw[r][c][1], xa[c], 0.0f);
+      g[r] = fmaf(pg, e8m0_to_f32(gsc[r][c]) * live[c], g[r]);
+      u[r] = fmaf(pu, e8m0_to_f32(usc[r][c]) * live[c], u[r]);
     }
   }
 #pragma unroll

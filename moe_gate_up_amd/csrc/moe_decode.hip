@@ -26,8 +26,9 @@ int check_shape(int B, int H, int I, int E, int k) {
   if (H % 32 || I % 32) return MOE_ERR_SHAPE;
   if (H > kMaxGateUpNbl * 64 * 32) return MOE_ERR_SHAPE;
   if ((long long)k * I > (long long)kMaxDownNbl * 64 * 32) return MOE_ERR_SHAPE;
-  // wave ids and slot indices are 32-bit
+  // wave ids, slot indices and buffer offsets are 32-bit
   if ((long long)B * k * I >= (1LL << 31) || (long long)B * H >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if ((long long)E * I * H >= (1LL << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -36,11 +37,14 @@ int blocks_per_lane(int blocks) { return (blocks + 63) / 64; }
 // ---------------------------------------------------------------- gate/up
 bool gate_up_allowed(int nbl, int r) { return (r == 1 || r == 2 || r == 4 || r == 8) && nbl * r <= 8; }
 
+// Rows per wave from a sweep on MI355X (graph-timed, H=2048/4096): more rows
+// per wave amortise the x slice and the reductions, but the grid must keep at
+// least ~12K wavefronts (12 per SIMD) to cover memory latency.
 int gate_up_default_rows(int B, int H, int I, int k) {
   const int nbl = blocks_per_lane(H / 32);
   const long long slots = (long long)B * k;
-  int r = 4;
-  while (r > 1 && (!gate_up_allowed(nbl, r) || slots * ((I + r - 1) / r) < 8192)) r /= 2;
+  int r = 8;
+  while (r > 1 && (!gate_up_allowed(nbl, r) || slots * ((I + r - 1) / r) < 12288)) r /= 2;
   return r;
 }
 
@@ -112,10 +116,12 @@ bool down_allowed(int nbl, int r) {
   return (r == 1 || r == 2 || r == 4 || r == 8) && nbl >= 1 && nbl <= kMaxDownNbl && nbl * (8 * r + 16) <= 192;
 }
 
+// The down wave streams k rows per output, so far fewer wavefronts suffice:
+// the sweep favours the largest register-feasible R with >= 1024 wavefronts.
 int down_default_rows(int B, int H, int I, int k) {
   const int nbl = blocks_per_lane(k * I / 32);
-  int r = 4;
-  while (r > 1 && (!down_allowed(nbl, r) || (long long)B * ((H + r - 1) / r) < 8192)) r /= 2;
+  int r = 8;
+  while (r > 1 && (!down_allowed(nbl, r) || (long long)B * ((H + r - 1) / r) < 1024)) r /= 2;
   return r;
 }
 
@@ -240,10 +246,10 @@ int moe_decode_copy_peak(const void* src, void* dst, size_t bytes, void* stream)
   if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_ALIGN;
   if (overlaps(src, bytes, dst, bytes)) return MOE_ERR_ALIAS;
   const size_t n = bytes / 16;
-  const size_t want = (n + 256 * 4 - 1) / (256 * 4);
-  const dim3 grid((unsigned)(want < 4096 ? want : 4096));
+  const size_t want = (n + moe::kPeakThreads - 1) / moe::kPeakThreads;
+  const dim3 grid((unsigned)(want < moe::kPeakMaxBlocks ? want : moe::kPeakMaxBlocks));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(moe::copy_peak_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(moe::copy_peak_kernel, grid, dim3(moe::kPeakThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const moe::u32x4*>(src), static_cast<moe::u32x4*>(dst), n);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
@@ -253,10 +259,10 @@ int moe_decode_read_peak(const void* src, size_t bytes, void* sink, void* stream
   if (bytes == 0 || bytes % 16) return MOE_ERR_SHAPE;
   if (!aligned(src, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
   const size_t n = bytes / 16;
-  const size_t want = (n + 256 * 4 - 1) / (256 * 4);
-  const dim3 grid((unsigned)(want < 4096 ? want : 4096));
+  const size_t want = (n + moe::kPeakThreads - 1) / moe::kPeakThreads;
+  const dim3 grid((unsigned)(want < moe::kPeakMaxBlocks ? want : moe::kPeakMaxBlocks));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(moe::read_peak_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(moe::read_peak_kernel, grid, dim3(moe::kPeakThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const moe::u32x4*>(src), n, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -23,13 +23,30 @@ struct alignas(16) u32x4 {
   uint32_t v[4];
 };
 
-// 16-byte global load.
-__device__ __forceinline__ u32x4 load16(const void* p) {
+// Buffer resources: a tensor's base address and byte size live in scalar
+// registers and every load is base + per-lane 32-bit offset + wave-uniform
+// 32-bit offset, so no per-lane 64-bit address arithmetic is needed.  (The
+// third dword selects a 32-bit data format, as raw buffer loads on gfx9-family
+// chips require.)  Offsets must stay below 2^32; the host checks tensor sizes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// 16 bytes at base + voff + soff.
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  v4u t = *reinterpret_cast<const v4u*>(p);
-  u32x4 r;
-  r.v[0] = t[0]; r.v[1] = t[1]; r.v[2] = t[2]; r.v[3] = t[3];
-  return r;
+  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  u32x4 o;
+  o.v[0] = t[0]; o.v[1] = t[1]; o.v[2] = t[2]; o.v[3] = t[3];
+  return o;
+}
+
+// One byte at base + voff + soff, zero-extended.
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
 // E4M3 bytes 0,1 (hi=false) or 2,3 (hi=true) of `word` -> bf16 pair (exact).
@@ -100,6 +117,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu(float g) {
   return g / (1.0f + __expf(-g));
+}
+
+// MI355X dispatches workgroup g to XCD (g mod 8); each XCD has its own L2.
+// Remap the hardware workgroup id to a logical one so that every XCD works
+// through one contiguous range of logical workgroups: work that shares weight
+// rows and is adjacent in logical order then shares one L2.  Bijective on
+// [0, G) for any G.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous_block(int g, int G) {
+  const int x = g % kXcds, i = g / kXcds;
+  const int q = G / kXcds, rem = G % kXcds;
+  return (x < rem) ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
 }
 
 __device__ __forceinline__ float qnan() { return __builtin_bit_cast(float, 0x7FC00000u); }

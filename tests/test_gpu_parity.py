@@ -220,6 +220,34 @@ def test_nondefault_stream(dev, s1):
     check(h, y, h_ref, y_ref, 4, 8, "stream")
 
 
+def test_graph_replay_matches_eager(dev, s1):
+    """Both kernels captured into one HIP graph; every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    B, k = 6, 8
+    x = mi.make_x(99, B, s1.H)
+    ids, w = mi.route_uniform(99, B, s1.E, k)
+    xd, idd, wdv = _t(x, dev), _t(ids, dev), _t(w, dev)
+    h = torch.empty((B, k, s1.I), dtype=torch.int16, device=dev)
+    y = torch.empty((B, s1.H), dtype=torch.int16, device=dev)
+    mg.moe_decode_gate_up(xd, idd, s1.wg, s1.sg, s1.wu, s1.su, h)
+    mg.moe_decode_down(h, idd, wdv, s1.wd, s1.sd, y)
+    torch.cuda.synchronize()
+    h_eager, y_eager = h.clone(), y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mg.moe_decode_gate_up(xd, idd, s1.wg, s1.sg, s1.wu, s1.su, h)
+        mg.moe_decode_down(h, idd, wdv, s1.wd, s1.sd, y)
+    for rep in range(4):
+        h.fill_(-1)
+        y.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_eager) and torch.equal(y, y_eager), rep
+    h_ref, y_ref = oracle.layer(x, ids, w, *s1.host())
+    check(h.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16), h_ref, y_ref, B, k, "graph")
+
+
 def test_empty_batch(dev, s1):
     x = torch.empty((0, s1.H), dtype=torch.int16, device=dev)
     ids = torch.empty((0, 8), dtype=torch.int32, device=dev)
