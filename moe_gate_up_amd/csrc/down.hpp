@@ -6,24 +6,29 @@
 //
 // MI355X mapping.  One 64-lane wavefront owns R consecutive output dimensions
 // of one token.  The k down rows of one output are treated as one
-// concatenated reduction of k*I elements (k*I/32 MX blocks): lane l owns
-// blocks l, l+64, ..., each of which lies inside one expert's row, so a lane
-// folds (router weight x block scale) into a single multiplier per block.  At
-// I=768 a row is 24 blocks and the 192 blocks of 8 experts spread evenly over
-// 64 lanes (3 each), which 16-byte loads per lane could not do for a single
-// 768-byte row.  h[b] is loaded once per wave and reused for the R outputs.
-// Straight-line code with buffer loads (scalar base, 32-bit lane offset,
-// scalar row offset); every load is issued before the first arithmetic.
-// Grid order: wave id = tile * B + b (tile slowest), with workgroups remapped
-// so that each XCD runs a contiguous range of tiles: tokens that share an
-// expert read its rows at about the same time on the same XCD (L2 hits).
+// concatenated reduction of k*I elements, read in passes of 1024 elements:
+// in pass c lane l takes the 16 elements at 1024c + 16l, which lie inside one
+// expert's row (rows are multiples of 32 elements), so each lane folds
+// (router weight x block scale) into a single multiplier per chunk, and each
+// load instruction covers whole cache lines of at most two rows.  At I=768 a
+// single row is too short for 64 lanes x 16 bytes; the 6144 concatenated
+// elements of 8 experts are 6 passes.  h[b] is loaded once per wave and
+// reused for the R outputs.  Straight-line code with buffer loads (scalar
+// base, 32-bit lane offset, scalar row offset); every load is issued before
+// the first arithmetic.
+//
+// Grid order: tile-major in groups of 4 tiles (wave id = (group, b, tile in
+// group)), with workgroups remapped so that each XCD runs a contiguous range
+// of groups: tokens that share an expert read its rows at about the same time
+// on the same XCD (L2 hits), and a workgroup reads 4*R consecutive rows of
+// each of its token's experts.
 #pragma once
 
 #include "prims.hpp"
 
 namespace moe {
 
-template <int NBL, int R>
+template <int NP, int R>
 __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
     const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd,
@@ -32,58 +37,77 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
   // wave-uniform: keep the index math in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
   if (wave >= o_tiles * B) return;
-  const int tile = __builtin_amdgcn_readfirstlane(wave / B);   // VALU division, uniform result
-  const int b = wave - tile * B;
+  // (H/R is a multiple of 4 because H is a multiple of 32 and R <= 8)
+  const int grp = __builtin_amdgcn_readfirstlane(wave / (4 * B));   // VALU division, uniform result
+  const int rem = wave - grp * 4 * B;
+  const int b = rem >> 2;
+  const int tile = grp * 4 + (rem & 3);
   const int o0 = tile * R;
   const int nb_row = I >> 5;          // MX blocks per down row
-  const int nb_tot = k * nb_row;      // blocks of the k concatenated rows
+  const int n_tot = k * I;            // elements of the k concatenated rows
 
   const uint32_t wbytes = (uint32_t)E * (uint32_t)H * (uint32_t)I;   // < 2^32, checked on the host
   const rsrc_t wr = make_rsrc(wd, wbytes), sr = make_rsrc(sd, wbytes / 32);
   const rsrc_t hr = make_rsrc(h, (uint64_t)B * k * I * 2);
   const rsrc_t idr = make_rsrc(ids, (uint64_t)B * k * 4), twr = make_rsrc(tw, (uint64_t)B * k * 4);
 
-  // lane block q of the concatenated rows: slot j = q / nb_row, block qb within the row.
-  // Lanes past the end re-read the last block and fold it with weight 0.
-  uint32_t woff[NBL], soff[NBL], hoff[NBL];
-  float fold[NBL];
+  // h[b] does not depend on the routing: issue its loads first
+  const uint32_t hbase = (uint32_t)b * (uint32_t)n_tot * 2u;
+  uint32_t off[NP];
+  u32x4 ha[NP][2];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    off[c] = (uint32_t)min(1024 * c + 16 * lane, n_tot - 16);   // clamped duplicates fold with weight 0
+    ha[c][0] = bload16(hr, off[c] * 2u, hbase);
+    ha[c][1] = bload16(hr, off[c] * 2u + 16u, hbase);
+  }
+
+  // slot j = off / I of each chunk: its expert, router weight and row offsets.
+  // One division for pass 0; later passes step by 1024 = step_j * I + step_w.
+  const int step_j = 1024 / I, step_w = 1024 - (1024 / I) * I;
+  int j = (16 * lane) / I;
+  int within = 16 * lane - j * I;
+  uint32_t woff[NP], soff[NP];
+  float fold[NP];
+  int bias[NP];
   bool any_bad = false;
 #pragma unroll
-  for (int c = 0; c < NBL; ++c) {
-    const int q_raw = lane + 64 * c;
-    const int q = min(q_raw, nb_tot - 1);
-    const int j = q / nb_row;
-    const int qb = q - j * nb_row;
+  for (int c = 0; c < NP; ++c) {
+    if (c > 0) {
+      j += step_j;
+      within += step_w;
+      if (within >= I) {
+        within -= I;
+        j += 1;
+      }
+    }
+    const bool live = (1024 * c + 16 * lane) < n_tot;
+    if (!live) {   // clamped duplicate of the last chunk
+      j = k - 1;
+      within = I - 16;
+    }
     const uint32_t slot = (uint32_t)(b * k + j);
     const int e_raw = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, slot * 4u, 0, 0));
     const bool bad = (unsigned)e_raw >= (unsigned)E;
     any_bad |= bad;
     const uint32_t row0 = (uint32_t)(bad ? 0 : e_raw) * (uint32_t)H;   // row (e, o=0)
-    woff[c] = row0 * (uint32_t)I + (uint32_t)qb * 32u;
-    soff[c] = row0 * (uint32_t)nb_row + (uint32_t)qb;
-    hoff[c] = (uint32_t)q * 64u;   // h[b] is [k, I] contiguous: block q = bytes [64q, 64q+64)
+    woff[c] = row0 * (uint32_t)I + (uint32_t)within;
+    soff[c] = row0 * (uint32_t)nb_row + (uint32_t)(within >> 5);
     const float wj = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(twr, slot * 4u, 0, 0));
-    fold[c] = q_raw < nb_tot ? wj : 0.0f;
+    fold[c] = wj;
+    bias[c] = live ? kLiveChunk : kDeadChunk;   // zero the clamped duplicates
   }
   const bool bad_token = __builtin_amdgcn_ballot_w64(any_bad) != 0;
 
-  const uint32_t hbase = (uint32_t)b * (uint32_t)k * (uint32_t)I * 2u;
-  u32x4 ha[NBL][4];
-#pragma unroll
-  for (int c = 0; c < NBL; ++c)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ha[c][t] = bload16(hr, hoff[c] + 16u * t, hbase);
-
-  u32x4 w[R][NBL][2];
-  uint32_t sc[R][NBL];
+  u32x4 w[R][NP];
+  uint32_t sc[R][NP];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t o = (uint32_t)min(o0 + r, H - 1);   // ragged last tile: clamp, not stored
     const uint32_t wo = o * (uint32_t)I, so = o * (uint32_t)nb_row;
 #pragma unroll
-    for (int c = 0; c < NBL; ++c) {
-      w[r][c][0] = bload16(wr, woff[c], wo);
-      w[r][c][1] = bload16(wr, woff[c] + 16u, wo);
+    for (int c = 0; c < NP; ++c) {
+      w[r][c] = bload16(wr, woff[c], wo);
       sc[r][c] = bload8(sr, soff[c], so);
     }
   }
@@ -92,14 +116,17 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
   __builtin_amdgcn_sched_barrier(0);
 
   float acc[R];
+  uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code among output r's rows
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     acc[r] = 0.0f;
+    uint64_t nan_lanes = 0;
 #pragma unroll
-    for (int c = 0; c < NBL; ++c) {
-      const float p = block_dot(w[r][c][0], w[r][c][1], ha[c], 0.0f);
-      acc[r] = fmaf(p, fold[c] * e8m0_to_f32(sc[r][c]), acc[r]);
+    for (int c = 0; c < NP; ++c) {
+      acc[r] = fmaf(apply_e8m0(chunk_dot(w[r][c], ha[c], 0.0f), sc[r][c], bias[c]), fold[c], acc[r]);
+      nan_lanes |= nan_scale_lanes(sc[r][c]);
     }
+    nan_rows |= (uint64_t)(nan_lanes != 0) << r;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum_row3(acc[r]);
@@ -109,8 +136,10 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
   float v = acc[0];
 #pragma unroll
   for (int r = 1; r < R; ++r) v = (r_out == r) ? acc[r] : v;
-  if (r_out >= 0 && r_out < R && o0 + r_out < H)
-    y[(size_t)b * H + o0 + r_out] = f32_to_bf16_rne(bad_token ? qnan() : v);
+  if (r_out >= 0 && r_out < R && o0 + r_out < H) {
+    const bool nan_out = bad_token || ((nan_rows >> r_out) & 1);
+    y[(size_t)b * H + o0 + r_out] = f32_to_bf16_rne(nan_out ? qnan() : v);
+  }
 }
 
 }  // namespace moe

@@ -5,16 +5,17 @@
 // SiLU(gate) * up is written once as bf16.
 //
 // MI355X mapping.  One 64-lane wavefront owns R consecutive neurons of one
-// (b, j) slot.  Lane l owns the 32-element MX blocks l, l+64, ... of a row, so
-// each lane needs exactly one E8M0 scale byte per row and block, and the 64
-// lanes together cover 2048 contiguous bytes per row (two 16-byte loads per
-// lane per block).  The lane's slice of x[b] is loaded once and reused for the
-// R gate rows and R up rows.  The code is straight-line: every load of the
-// wave is issued before the first arithmetic, so each wave keeps R*4 KB in
-// flight; lanes past the end of a short row re-read the row's last block and
-// contribute zero.  Loads are buffer loads: scalar base, 32-bit lane offset,
-// scalar row offset.  Per-lane partial sums are reduced across the wave with DPP row
-// operations, not LDS.
+// (b, j) slot.  A row is read in passes of 1024 contiguous bytes: in pass c
+// lane l loads the 16 bytes at 1024c + 16l, so every load instruction of the
+// wave covers eight whole 128-byte cache lines (the contiguous access the
+// pages' copy-kernel peak is measured with).  Two neighbouring lanes share
+// the E8M0 scale of their 32-element block.  The lane's slice of x[b] is
+// loaded once and reused for the R gate rows and R up rows.  The code is
+// straight-line: every load of the wave is issued before the first
+// arithmetic, so each wave keeps R*4 KB in flight; lanes past the end of a
+// row re-read its last chunk and contribute zero.  Loads are buffer loads:
+// scalar base, 32-bit lane offset, scalar row offset.  Per-lane partial sums
+// are reduced across the wave with DPP row operations, not LDS.
 //
 // Grid order: wave id = tile * (B*k) + slot, tile (neuron group) slowest, and
 // workgroups are remapped so that each XCD runs a contiguous range of tiles.
@@ -26,7 +27,7 @@
 
 namespace moe {
 
-template <int NBL, int R>
+template <int NCH, int R>
 __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
@@ -47,14 +48,15 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   const bool bad = (unsigned)e_raw >= (unsigned)E;
   const int e = bad ? 0 : e_raw;
 
-  // block of this lane in pass c, clamped to the row; `live` zeroes the clamped duplicates
-  uint32_t qb[NBL];
-  float live[NBL];
+  // element offset of this lane's 16-element chunk in pass c, clamped to the
+  // row; the scale bias zeroes the clamped duplicates
+  uint32_t off[NCH];
+  int bias[NCH];
 #pragma unroll
-  for (int c = 0; c < NBL; ++c) {
-    const int q = lane + 64 * c;
-    qb[c] = (uint32_t)min(q, nblk - 1);
-    live[c] = q < nblk ? 1.0f : 0.0f;
+  for (int c = 0; c < NCH; ++c) {
+    const int o = 1024 * c + 16 * lane;
+    off[c] = (uint32_t)min(o, H - 16);
+    bias[c] = o < H ? kLiveChunk : kDeadChunk;
   }
 
   const uint32_t wbytes = (uint32_t)E * (uint32_t)I * (uint32_t)H;   // < 2^32, checked on the host
@@ -62,28 +64,26 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   const rsrc_t gr = make_rsrc(wg, wbytes), ur = make_rsrc(wu, wbytes);
   const rsrc_t gsr = make_rsrc(sg, wbytes / 32), usr = make_rsrc(su, wbytes / 32);
 
-  // x[b] slice: block q covers elements [32q, 32q+32) = bytes [64q, 64q+64)
   const uint32_t xoff = (uint32_t)b * (uint32_t)H * 2u;
-  u32x4 xa[NBL][4];
+  u32x4 xa[NCH][2];
 #pragma unroll
-  for (int c = 0; c < NBL; ++c)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) xa[c][t] = bload16(xr, qb[c] * 64u + 16u * t, xoff);
+  for (int c = 0; c < NCH; ++c) {
+    xa[c][0] = bload16(xr, off[c] * 2u, xoff);
+    xa[c][1] = bload16(xr, off[c] * 2u + 16u, xoff);
+  }
 
-  u32x4 gw[R][NBL][2], uw[R][NBL][2];
-  uint32_t gsc[R][NBL], usc[R][NBL];
+  u32x4 gw[R][NCH], uw[R][NCH];
+  uint32_t gsc[R][NCH], usc[R][NCH];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t row = (uint32_t)(e * I + min(n0 + r, I - 1));   // ragged last tile: clamp, not stored
     const uint32_t woff = row * (uint32_t)H, soff = row * (uint32_t)nblk;
 #pragma unroll
-    for (int c = 0; c < NBL; ++c) {
-      gw[r][c][0] = bload16(gr, qb[c] * 32u, woff);
-      gw[r][c][1] = bload16(gr, qb[c] * 32u + 16u, woff);
-      uw[r][c][0] = bload16(ur, qb[c] * 32u, woff);
-      uw[r][c][1] = bload16(ur, qb[c] * 32u + 16u, woff);
-      gsc[r][c] = bload8(gsr, qb[c], soff);
-      usc[r][c] = bload8(usr, qb[c], soff);
+    for (int c = 0; c < NCH; ++c) {
+      gw[r][c] = bload16(gr, off[c], woff);
+      uw[r][c] = bload16(ur, off[c], woff);
+      gsc[r][c] = bload8(gsr, off[c] >> 5, soff);
+      usc[r][c] = bload8(usr, off[c] >> 5, soff);
     }
   }
 
@@ -91,17 +91,19 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   __builtin_amdgcn_sched_barrier(0);
 
   float g[R], u[R];
+  uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code in row r
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     g[r] = 0.0f;
     u[r] = 0.0f;
+    uint64_t nan_lanes = 0;
 #pragma unroll
-    for (int c = 0; c < NBL; ++c) {
-      const float pg = block_dot(gw[r][c][0], gw[r][c][1], xa[c], 0.0f);
-      const float pu = block_dot(uw[r][c][0], uw[r][c][1], xa[c], 0.0f);
-      g[r] = fmaf(pg, e8m0_to_f32(gsc[r][c]) * live[c], g[r]);
-      u[r] = fmaf(pu, e8m0_to_f32(usc[r][c]) * live[c], u[r]);
+    for (int c = 0; c < NCH; ++c) {
+      g[r] += apply_e8m0(chunk_dot(gw[r][c], xa[c], 0.0f), gsc[r][c], bias[c]);
+      u[r] += apply_e8m0(chunk_dot(uw[r][c], xa[c], 0.0f), usc[r][c], bias[c]);
+      nan_lanes |= nan_scale_lanes(gsc[r][c]) | nan_scale_lanes(usc[r][c]);
     }
+    nan_rows |= (uint64_t)(nan_lanes != 0) << r;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     uv = (r_out == r) ? u[r] : uv;
   }
   if (r_out >= 0 && r_out < R && n0 + r_out < I) {
-    const float hv = bad ? qnan() : silu(gv) * uv;
+    const bool nan_out = bad || ((nan_rows >> r_out) & 1);
+    const float hv = nan_out ? qnan() : silu(gv) * uv;
     h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(hv);
   }
 }

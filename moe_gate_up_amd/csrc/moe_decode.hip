@@ -3,6 +3,8 @@
 // stated in include/moe_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "moe_decode.h"
 #include "down.hpp"
 #include "gate_up.hpp"
@@ -11,8 +13,8 @@
 namespace {
 
 constexpr int kWavesPerBlock = 4;   // 256 threads = 4 independent 64-lane wavefronts
-constexpr int kMaxGateUpNbl = 4;    // H <= 4 * 64 * 32 = 8192
-constexpr int kMaxDownNbl = 8;      // k * I <= 8 * 64 * 32 = 16384
+constexpr int kMaxGateUpPasses = 8;   // H <= 8 passes of 1024 elements = 8192
+constexpr int kMaxDownPasses = 16;    // k * I <= 16 passes of 1024 elements = 16384
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -24,34 +26,41 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int check_shape(int B, int H, int I, int E, int k) {
   if (B < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_SHAPE;
   if (H % 32 || I % 32) return MOE_ERR_SHAPE;
-  if (H > kMaxGateUpNbl * 64 * 32) return MOE_ERR_SHAPE;
-  if ((long long)k * I > (long long)kMaxDownNbl * 64 * 32) return MOE_ERR_SHAPE;
+  if (H > kMaxGateUpPasses * 1024) return MOE_ERR_SHAPE;
+  if ((long long)k * I > (long long)kMaxDownPasses * 1024) return MOE_ERR_SHAPE;
   // wave ids, slot indices and buffer offsets are 32-bit
   if ((long long)B * k * I >= (1LL << 31) || (long long)B * H >= (1LL << 31)) return MOE_ERR_SHAPE;
   if ((long long)E * I * H >= (1LL << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
-int blocks_per_lane(int blocks) { return (blocks + 63) / 64; }
+// passes of 1024 elements (64 lanes x 16) over a reduction of n elements
+int passes(long long n) { return (int)((n + 1023) / 1024); }
 
 // ---------------------------------------------------------------- gate/up
-bool gate_up_allowed(int nbl, int r) { return (r == 1 || r == 2 || r == 4 || r == 8) && nbl * r <= 8; }
+// register budget: R rows x NCH passes x (gate + up) x 4 VGPRs of weights
+constexpr bool gate_up_fits(int nch, int r) { return nch * r <= 16; }
+bool gate_up_allowed(int nch, int r) {
+  return (r == 1 || r == 2 || r == 4 || r == 8) && nch >= 1 && nch <= kMaxGateUpPasses && gate_up_fits(nch, r);
+}
 
-// Rows per wave from a sweep on MI355X (graph-timed, H=2048/4096): more rows
-// per wave amortise the x slice and the reductions, but the grid must keep at
-// least ~12K wavefronts (12 per SIMD) to cover memory latency.
+// Rows per wave from a graph-timed sweep on MI355X (H = 2048 and 4096): more
+// rows per wave amortise the x slice and the reductions, but the grid must
+// keep at least ~16K wavefronts to cover memory latency, and beyond
+// R * passes = 8 the register file limits occupancy to two waves per SIMD,
+// which measured slower.
 int gate_up_default_rows(int B, int H, int I, int k) {
-  const int nbl = blocks_per_lane(H / 32);
+  const int nch = passes(H);
   const long long slots = (long long)B * k;
   int r = 8;
-  while (r > 1 && (!gate_up_allowed(nbl, r) || slots * ((I + r - 1) / r) < 12288)) r /= 2;
+  while (r > 1 && (!gate_up_allowed(nch, r) || nch * r > 8 || slots * ((I + r - 1) / r) < 16384)) r /= 2;
   return r;
 }
 
-template <int NBL, int R>
+template <int NCH, int R>
 void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
                       const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
-  hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NBL, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+  hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
                      static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
                      tiles);
 }
@@ -59,29 +68,33 @@ void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* i
 using GateUpLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
                               const uint8_t*, const uint8_t*, void*, int, int, int, int, int, int);
 
-template <int NBL, int R>
+template <int NCH, int R>
 GateUpLaunch gate_up_fn() {
-  if constexpr (NBL * R <= 8) return launch_gate_up_t<NBL, R>;
+  if constexpr (gate_up_fits(NCH, R)) return launch_gate_up_t<NCH, R>;
   else return nullptr;
 }
 
-template <int NBL>
+template <int NCH>
 GateUpLaunch pick_gate_up_r(int r) {
   switch (r) {
-    case 1: return gate_up_fn<NBL, 1>();
-    case 2: return gate_up_fn<NBL, 2>();
-    case 4: return gate_up_fn<NBL, 4>();
-    case 8: return gate_up_fn<NBL, 8>();
+    case 1: return gate_up_fn<NCH, 1>();
+    case 2: return gate_up_fn<NCH, 2>();
+    case 4: return gate_up_fn<NCH, 4>();
+    case 8: return gate_up_fn<NCH, 8>();
   }
   return nullptr;
 }
 
-GateUpLaunch pick_gate_up(int nbl, int r) {
-  switch (nbl) {
+GateUpLaunch pick_gate_up(int nch, int r) {
+  switch (nch) {
     case 1: return pick_gate_up_r<1>(r);
     case 2: return pick_gate_up_r<2>(r);
     case 3: return pick_gate_up_r<3>(r);
     case 4: return pick_gate_up_r<4>(r);
+    case 5: return pick_gate_up_r<5>(r);
+    case 6: return pick_gate_up_r<6>(r);
+    case 7: return pick_gate_up_r<7>(r);
+    case 8: return pick_gate_up_r<8>(r);
   }
   return nullptr;
 }
@@ -98,10 +111,10 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
   if (overlaps(h, hb, x, (size_t)B * H * 2) || overlaps(h, hb, ids, (size_t)B * k * 4) || overlaps(h, hb, wg, wb) ||
       overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
     return MOE_ERR_ALIAS;
-  const int nbl = blocks_per_lane(H / 32);
+  const int nch = passes(H);
   if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
-  if (!gate_up_allowed(nbl, rows)) return MOE_ERR_ARG;
-  GateUpLaunch fn = pick_gate_up(nbl, rows);
+  if (!gate_up_allowed(nch, rows)) return MOE_ERR_ARG;
+  GateUpLaunch fn = pick_gate_up(nch, rows);
   if (!fn) return MOE_ERR_ARG;
   const int tiles = (I + rows - 1) / rows;
   const long long waves = (long long)tiles * B * k;
@@ -112,58 +125,57 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
 }
 
 // ---------------------------------------------------------------- down
-bool down_allowed(int nbl, int r) {
-  return (r == 1 || r == 2 || r == 4 || r == 8) && nbl >= 1 && nbl <= kMaxDownNbl && nbl * (8 * r + 16) <= 192;
+// register budget per pass: R weight chunks (4 VGPRs) + R scales + h (8 VGPRs)
+constexpr bool down_fits(int np, int r) { return np * (5 * r + 8) <= 224; }
+bool down_allowed(int np, int r) {
+  return (r == 1 || r == 2 || r == 4 || r == 8) && np >= 1 && np <= kMaxDownPasses && down_fits(np, r);
 }
 
 // The down wave streams k rows per output, so far fewer wavefronts suffice:
 // the sweep favours the largest register-feasible R with >= 1024 wavefronts.
 int down_default_rows(int B, int H, int I, int k) {
-  const int nbl = blocks_per_lane(k * I / 32);
+  const int np = passes((long long)k * I);
   int r = 8;
-  while (r > 1 && (!down_allowed(nbl, r) || (long long)B * ((H + r - 1) / r) < 1024)) r /= 2;
+  while (r > 1 && (!down_allowed(np, r) || (long long)B * ((H + r - 1) / r) < 1024)) r /= 2;
   return r;
 }
 
-template <int NBL, int R>
+template <int NP, int R>
 void launch_down_t(dim3 grid, hipStream_t st, const void* h, const int32_t* ids, const float* tw, const uint8_t* wd,
                    const uint8_t* sd, void* y, int B, int H, int I, int E, int k, int tiles) {
-  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NBL, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
                      static_cast<const uint16_t*>(h), ids, tw, wd, sd, static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
 }
 
 using DownLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const float*, const uint8_t*,
                             const uint8_t*, void*, int, int, int, int, int, int);
 
-template <int NBL, int R>
+template <int NP, int R>
 DownLaunch down_fn() {
-  if constexpr (NBL * (8 * R + 16) <= 192) return launch_down_t<NBL, R>;
+  if constexpr (down_fits(NP, R)) return launch_down_t<NP, R>;
   else return nullptr;
 }
 
-template <int NBL>
+template <int NP>
 DownLaunch pick_down_r(int r) {
   switch (r) {
-    case 1: return down_fn<NBL, 1>();
-    case 2: return down_fn<NBL, 2>();
-    case 4: return down_fn<NBL, 4>();
-    case 8: return down_fn<NBL, 8>();
+    case 1: return down_fn<NP, 1>();
+    case 2: return down_fn<NP, 2>();
+    case 4: return down_fn<NP, 4>();
+    case 8: return down_fn<NP, 8>();
   }
   return nullptr;
 }
 
-DownLaunch pick_down(int nbl, int r) {
-  switch (nbl) {
-    case 1: return pick_down_r<1>(r);
-    case 2: return pick_down_r<2>(r);
-    case 3: return pick_down_r<3>(r);
-    case 4: return pick_down_r<4>(r);
-    case 5: return pick_down_r<5>(r);
-    case 6: return pick_down_r<6>(r);
-    case 7: return pick_down_r<7>(r);
-    case 8: return pick_down_r<8>(r);
-  }
-  return nullptr;
+template <int... NPs>
+DownLaunch pick_down_np(int np, int r, std::integer_sequence<int, NPs...>) {
+  DownLaunch fn = nullptr;
+  ((np == NPs + 1 ? (fn = pick_down_r<NPs + 1>(r), 0) : 0), ...);
+  return fn;
+}
+
+DownLaunch pick_down(int np, int r) {
+  return pick_down_np(np, r, std::make_integer_sequence<int, kMaxDownPasses>{});
 }
 
 int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t* wd, const uint8_t* sd, void* y,
@@ -178,10 +190,10 @@ int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t*
   if (overlaps(y, yb, h, (size_t)B * k * I * 2) || overlaps(y, yb, ids, (size_t)B * k * 4) ||
       overlaps(y, yb, tw, (size_t)B * k * 4) || overlaps(y, yb, wd, wb) || overlaps(y, yb, sd, wb / 32))
     return MOE_ERR_ALIAS;
-  const int nbl = blocks_per_lane(k * I / 32);
+  const int np = passes((long long)k * I);
   if (rows == 0) rows = down_default_rows(B, H, I, k);
-  if (!down_allowed(nbl, rows)) return MOE_ERR_ARG;
-  DownLaunch fn = pick_down(nbl, rows);
+  if (!down_allowed(np, rows)) return MOE_ERR_ARG;
+  DownLaunch fn = pick_down(np, rows);
   if (!fn) return MOE_ERR_ARG;
   const int tiles = (H + rows - 1) / rows;
   const long long waves = (long long)tiles * B;

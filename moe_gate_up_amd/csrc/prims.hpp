@@ -62,25 +62,26 @@ __device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
 }
 
-// E8M0 code -> FP32 value 2^(s-127); 0 -> 2^-127 (FP32 subnormal), 0xFF -> NaN.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  uint32_t bits = s << 23;
-  bits = (s == 0u) ? 0x00400000u : bits;
-  bits = (s == 255u) ? 0x7FC00000u : bits;
-  return __builtin_bit_cast(float, bits);
+// Apply an E8M0 block scale to an FP32 partial sum: p * 2^(s + bias), one
+// v_ldexp_f32 (exact, subnormal results included).  bias is -127 for a real
+// chunk and kDeadChunk for a clamped duplicate, which makes its contribution
+// zero.  The NaN code 0xFF is not representable this way: callers collect
+// the lanes holding it with nan_scale_lanes() and force the output to NaN.
+constexpr int kLiveChunk = -127;
+constexpr int kDeadChunk = -512;
+__device__ __forceinline__ float apply_e8m0(float p, uint32_t s, int bias) {
+  return __builtin_ldexpf(p, (int)s + bias);
 }
+__device__ __forceinline__ uint64_t nan_scale_lanes(uint32_t s) { return __builtin_amdgcn_ballot_w64(s == 255u); }
 
-// Dot product of one 32-element MXFP8 block (w: 2 x 16 bytes of E4M3) with 32
-// bf16 activations (xa: 4 x 16 bytes), returned unscaled in FP32.
-__device__ __forceinline__ float block_dot(const u32x4& w0, const u32x4& w1, const u32x4* xa, float acc) {
+// Dot product of 16 E4M3 weights (w: 16 bytes) with 16 bf16 activations
+// (xa: 2 x 16 bytes), returned unscaled in FP32.
+__device__ __forceinline__ float chunk_dot(const u32x4& w, const u32x4* xa, float acc) {
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const uint32_t word = (d < 4) ? w0.v[d] : w1.v[d - 4];
-    // elements 4d..4d+3 of the block; activations are dwords 2d and 2d+1
-    const uint32_t x01 = xa[(2 * d) >> 2].v[(2 * d) & 3];
-    const uint32_t x23 = xa[(2 * d + 1) >> 2].v[(2 * d + 1) & 3];
-    acc = dot2(e4m3x2_to_bf16x2(word, false), as_bf16x2(x01), acc);
-    acc = dot2(e4m3x2_to_bf16x2(word, true), as_bf16x2(x23), acc);
+  for (int d = 0; d < 4; ++d) {
+    // weights 4d..4d+3; activations are dwords 2d and 2d+1 of the 8
+    acc = dot2(e4m3x2_to_bf16x2(w.v[d], false), as_bf16x2(xa[d >> 1].v[(2 * d) & 3]), acc);
+    acc = dot2(e4m3x2_to_bf16x2(w.v[d], true), as_bf16x2(xa[d >> 1].v[(2 * d + 1) & 3]), acc);
   }
   return acc;
 }

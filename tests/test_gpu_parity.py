@@ -100,10 +100,12 @@ SMALL = [
     (3, 2048, 96, 16, 8),
     (5, 256, 64, 8, 2),
     (2, 4096, 160, 8, 4),
-    (4, 2080, 800, 6, 3),     # 65 blocks per row (ragged second pass), I not a multiple of 8
-    (7, 32, 32, 4, 4),        # one block per row
-    (2, 6144, 96, 4, 2),      # three blocks per lane
-    (3, 1024, 1536, 8, 8),    # six blocks per lane in down
+    (4, 2080, 800, 6, 3),     # ragged last pass (2080 = 2 x 1024 + 32), k*I = 2400
+    (7, 32, 32, 4, 4),        # one 32-element block per row: most lanes clamped
+    (2, 6144, 96, 4, 2),      # six passes over a row
+    (3, 1024, 1536, 8, 8),    # twelve passes in down
+    (2, 8192, 64, 3, 2),      # the widest supported rows
+    (1, 2048, 2048, 8, 8),    # the longest supported down reduction (k*I = 16384)
 ]
 
 
@@ -117,9 +119,10 @@ def small_layers(dev):
 def test_small_shapes_all_variants(dev, small_layers, shape, rows):
     B, H, I, E, k = shape
     D = small_layers[shape]
-    nbl_gu, nbl_dn = -(-H // 2048), -(-(k * I) // 2048)
-    rows_gu = rows if rows is None or rows * nbl_gu <= 8 else None
-    rows_dn = rows if rows is None or nbl_dn * (8 * rows + 16) <= 192 else None
+    # register-feasible variants only (passes of 1024 elements per lane group)
+    n_gu, n_dn = -(-H // 1024), -(-(k * I) // 1024)
+    rows_gu = rows if rows is None or rows * n_gu <= 16 else None
+    rows_dn = rows if rows is None or n_dn * (5 * rows + 8) <= 224 else None
     x = mi.make_x(7, B, H)
     ids, w = mi.route_uniform(7, B, E, k)
     h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn)
