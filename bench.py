@@ -95,6 +95,7 @@ def main():
     ap.add_argument("--sweep", default="1,2,4,8,16,32", help="batch sizes for the sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the routing-stress, 48-layer and wide-shape runs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     args = ap.parse_args()
 
@@ -164,50 +165,54 @@ def main():
     log(f"copy peak {copy_gbps:.0f} GB/s (read+write), read peak {read_gbps:.0f} GB/s")
 
     # ---------------------------------------------------------------- routed steps
-    def make_batch(B, n, seed):
+    def make_batch(shape, B, n, kind, seed):
+        H_, I_, E_, k_ = shape
         xs, ids_l, ws, info = [], [], [], []
         for r in range(n):
-            xs.append(mi.make_x(seed, B, H, it=r))
-            ids, w = mi.route_uniform(seed, B, E, k, it=r)
+            xs.append(mi.make_x(seed, B, H_, it=r))
+            ids, w = mi.make_routing(kind, seed, B, E_, k_, it=r)
             ids_l.append(ids)
             ws.append(w)
-            info.append(layer_bytes(ids, H, I, k))
+            info.append(layer_bytes(ids, H_, I_, k_))
         return (up(np.stack(xs)), up(np.stack(ids_l)), up(np.stack(ws)), info)
 
-    def run_steps(B, steps, warmup, n_rout):
-        """Time `steps` whole-layer steps (both kernels), then each kernel alone in a
-        back-to-back loop of `steps` launches (same weight copies and routings).
+    def run_steps(wcopies, shape, B, steps, warmup, n_rout, kind="uniform", seed=None, layers=1, kernels=True):
+        """Time `steps` steps; a step is `layers` whole-layer passes (both kernels),
+        layer l of a step reading weight copy l (cycled) with its own routing.
+        Then each kernel alone in a back-to-back loop of steps*layers launches.
 
         Each loop is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
         graph is replayed inside the timed region, so the figure is the GPU's time
         for the launches and not the Python launch overhead, which at small B
-        exceeds the kernels' own duration.  One eager pass runs first."""
-        xs, idss, wss, info = make_batch(B, n_rout, mi.routing_seed(2, B))
-        h = torch.empty((B, k, I), dtype=torch.int16, device=dev)
-        y = torch.empty((B, H), dtype=torch.int16, device=dev)
+        exceeds the kernels' own duration.  Warm-up passes run eagerly first."""
+        H_, I_, E_, k_ = shape
+        seed = mi.routing_seed(2, B) if seed is None else seed
+        xs, idss, wss, info = make_batch(shape, B, n_rout, kind, seed)
+        h = torch.empty((B, k_, I_), dtype=torch.int16, device=dev)
+        y = torch.empty((B, H_), dtype=torch.int16, device=dev)
 
         def gate_up(i):
-            wg, sg, wu, su, _, _ = copies[i % len(copies)]
+            wg, sg, wu, su, _, _ = wcopies[i % len(wcopies)]
             r = i % n_rout
             mg.moe_decode_gate_up(xs[r], idss[r], wg, sg, wu, su, h)
 
         def down(i):
-            _, _, _, _, wd, sd = copies[i % len(copies)]
+            _, _, _, _, wd, sd = wcopies[i % len(wcopies)]
             r = i % n_rout
             mg.moe_decode_down(h, idss[r], wss[r], wd, sd, y)
 
-        def step(i):
+        def layer(i):
             gate_up(i)
             down(i)
 
-        def timed(fn):
-            for i in range(warmup):
+        def timed(fn, n):
+            for i in range(warmup * layers):
                 fn(i)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for i in range(steps):
-                    fn(warmup + i)
+                for i in range(n):
+                    fn(warmup * layers + i)
             g.replay()   # untimed first replay
             torch.cuda.synchronize()
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -218,22 +223,31 @@ def main():
             torch.cuda.synchronize()
             return start.elapsed_time(end) / 1e3, time.perf_counter() - w0
 
-        t, wall = timed(step)
+        n = steps * layers
+        t, wall = timed(layer, n)
         # sanity: outputs are finite (parity itself is checked by the test suite)
         assert torch.isfinite(y.view(torch.bfloat16).float()).all().item()
-        t_gu, _ = timed(gate_up)
-        t_dn, _ = timed(down)
-        pick = [info[(warmup + i) % n_rout] for i in range(steps)]
+        pick = [info[(warmup * layers + i) % n_rout] for i in range(n)]
         byt = sum(d["total"] for d in pick)
-        gub = sum(d["gate_up"] for d in pick)
-        dnb = sum(d["down"] for d in pick)
-        return dict(B=B, seconds=t, wall_seconds=wall, bytes=byt, us_per_layer=t / steps * 1e6,
-                    GBps=byt / t / 1e9, distinct_experts=float(np.mean([d["distinct"] for d in info])),
-                    gate_up_us=t_gu / steps * 1e6, down_us=t_dn / steps * 1e6,
-                    gate_up_GBps=gub / t_gu / 1e9, down_GBps=dnb / t_dn / 1e9)
+        res = dict(B=B, seconds=t, wall_seconds=wall, bytes=byt, us_per_layer=t / n * 1e6,
+                   us_per_step=t / steps * 1e6, GBps=byt / t / 1e9,
+                   distinct_experts=float(np.mean([d["distinct"] for d in info])))
+        if kernels:
+            t_gu, _ = timed(gate_up, n)
+            t_dn, _ = timed(down, n)
+            gub = sum(d["gate_up"] for d in pick)
+            dnb = sum(d["down"] for d in pick)
+            res.update(gate_up_us=t_gu / n * 1e6, down_us=t_dn / n * 1e6,
+                       gate_up_GBps=gub / t_gu / 1e9, down_GBps=dnb / t_dn / 1e9)
+        return res
 
+    def brief(r, keys=("B", "us_per_layer", "us_per_step", "GBps", "frac_of_copy_peak", "distinct_experts",
+                       "gate_up_us", "down_us", "gate_up_GBps", "down_GBps", "routing", "layers")):
+        return {kk: (round(r[kk], 4) if isinstance(r[kk], float) else r[kk]) for kk in keys if kk in r}
+
+    S1 = (H, I, E, k)
     B = args.batch
-    main_res = run_steps(B, args.steps, args.warmup, args.routings)
+    main_res = run_steps(copies, S1, B, args.steps, args.warmup, args.routings)
     kern = main_res
     log(f"B={B}: {main_res['us_per_layer']:.2f} us/layer, {main_res['GBps']:.0f} GB/s effective "
         f"({main_res['GBps'] / copy_gbps:.1%} of copy peak)")
@@ -241,13 +255,62 @@ def main():
         f"down {kern['down_us']:.2f} us ({kern['down_GBps']:.0f} GB/s)")
 
     sweep = []
-    for b in [int(s) for s in args.sweep.split(",") if s.strip()]:
-        r = run_steps(b, args.sweep_steps, 10, args.routings)
+    for b in [int(v) for v in args.sweep.split(",") if v.strip()]:
+        r = run_steps(copies, S1, b, args.sweep_steps, 10, args.routings)
         r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
-        sweep.append({kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in r.items()
-                      if kk not in ("seconds", "wall_seconds", "bytes")})
+        sweep.append(brief(r))
         log(f"sweep B={b}: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s ({r['frac_of_copy_peak']:.1%}); "
             f"gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us")
+
+    extra = {}
+    if not args.no_configs:
+        # routing stress at B=32: Zipf(1.1) popularity, adversarial (ids >= 3 apart), contiguous control
+        c3 = []
+        for kind in ("zipf", "adversarial", "contiguous"):
+            r = run_steps(copies, S1, 32, args.sweep_steps, 10, args.routings, kind=kind,
+                          seed=mi.routing_seed(3, 32, kind))
+            r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
+            r["routing"] = kind
+            c3.append(brief(r))
+            log(f"routing {kind} B=32: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s "
+                f"({r['frac_of_copy_peak']:.1%}), {r['distinct_experts']:.1f} distinct experts")
+        extra["routing_stress_b32"] = c3
+
+        # 48-layer decode step: 48 weight copies at distinct addresses, fresh routing per layer
+        deep = [copies[i % len(copies)] if i < len(copies) else [t.clone() for t in first] for i in range(48)]
+        torch.cuda.synchronize()
+        c4 = []
+        for b in (1, 8, 32):
+            r = run_steps(deep, S1, b, 10, 2, 96, seed=4000, layers=48, kernels=False)
+            r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
+            r["layers"] = 48
+            c4.append(brief(r))
+            log(f"48-layer step B={b}: {r['us_per_step']:.1f} us/step, {r['us_per_layer']:.2f} us/layer, "
+                f"{r['GBps']:.0f} GB/s ({r['frac_of_copy_peak']:.1%})")
+        extra["decode_step_48_layers"] = c4
+        del deep
+        torch.cuda.empty_cache()
+
+        # wider expert shape: H=4096, I=1536, 8 layers
+        S2d = mi.SHAPES["S2"]
+        t0 = time.time()
+        L2 = mi.make_layer(mi.layer_seed(5, 0), S2d["H"], S2d["I"], S2d["E"])
+        wide = [[up(a) for a in (L2.w_gate, L2.s_gate, L2.w_up, L2.s_up, L2.w_down, L2.s_down)]]
+        del L2
+        wide += [[t.clone() for t in wide[0]] for _ in range(7)]
+        torch.cuda.synchronize()
+        log(f"wide layer ready in {time.time() - t0:.1f}s")
+        c5 = []
+        S2 = (S2d["H"], S2d["I"], S2d["E"], S2d["k"])
+        for b in (1, 16, 32, 64):
+            r = run_steps(wide, S2, b, args.sweep_steps // 2, 5, 32, seed=mi.routing_seed(5, b))
+            r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
+            c5.append(brief(r))
+            log(f"H=4096/I=1536 B={b}: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s "
+                f"({r['frac_of_copy_peak']:.1%}); gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us")
+        extra["wide_shape_h4096_i1536"] = c5
+        del wide
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -305,6 +368,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        **extra,
         "wall_seconds_timed": round(main_res["wall_seconds"], 4),
     }
     print(json.dumps(out), flush=True)

@@ -94,26 +94,44 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
                     void *y_out,
                     int B, int H, int I, int E, int k, void *stream);
 
+/* Kernel variants of the gate/up call.
+ *   MOE_GATE_UP_PER_SLOT: one wavefront per (R neurons, token slot) -- the
+ *     blog post's organisation, one output set per warp ("How the two kernels
+ *     work").  Best while few tokens share an expert.
+ *   MOE_GATE_UP_EXPERT_GROUPED: one wavefront per (R neurons, expert); it
+ *     finds the slots routed to its expert in topk_ids, reads and converts
+ *     the expert's rows once and produces h for every such slot.  Same
+ *     outputs; best once the batch routes several tokens to each expert.
+ *     Requires B*k <= 1024.
+ * The plain call uses MOE_GATE_UP_PER_SLOT, the faster of the two in every
+ * measured configuration. */
+#define MOE_GATE_UP_PER_SLOT 1
+#define MOE_GATE_UP_EXPERT_GROUPED 2
+
 /* Tuning variants of the two calls: the same contract and results within the
  * same tolerance, with the launch shape given explicitly instead of taken
- * from the built-in table.  rows_per_wave in {1, 2, 4, 8} is the number of
+ * from the built-in table.  variant: 0 = the table's choice, else one of the
+ * MOE_GATE_UP_* values.  rows_per_wave in {1, 2, 4, 8} is the number of
  * neurons (gate/up) or output dimensions (down) one 64-lane wavefront owns;
- * 0 selects the table's choice.  Other values return MOE_ERR_ARG. */
+ * 0 selects the table's choice.  Combinations beyond the register budget
+ * (rows x passes of 1024 elements: <= 16 per-slot, <= 8 grouped; down:
+ * passes x (5 rows + 8) <= 224) and unknown variants return MOE_ERR_ARG. */
 int moe_decode_gate_up_ex(const void *x, const int32_t *topk_ids,
                           const uint8_t *w_gate, const uint8_t *s_gate,
                           const uint8_t *w_up, const uint8_t *s_up,
                           void *h_out,
                           int B, int H, int I, int E, int k,
-                          int rows_per_wave, void *stream);
+                          int variant, int rows_per_wave, void *stream);
 int moe_decode_down_ex(const void *h, const int32_t *topk_ids, const float *topk_weights,
                        const uint8_t *w_down, const uint8_t *s_down,
                        void *y_out,
                        int B, int H, int I, int E, int k,
                        int rows_per_wave, void *stream);
 
-/* The launch shape the built-in table picks for a call (for reports):
- * writes rows_per_wave and the number of workgroups; returns 0 or a negative code. */
-int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int *rows_per_wave, int *workgroups);
+/* The launch the built-in table picks for a call (for reports): writes the
+ * variant (gate/up only), rows_per_wave and the number of workgroups;
+ * returns 0 or a negative code. */
+int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int *variant, int *rows_per_wave, int *workgroups);
 int moe_decode_down_plan(int B, int H, int I, int E, int k, int *rows_per_wave, int *workgroups);
 
 /* Bandwidth probes that set the denominator of the efficiency figure (blog

@@ -8,6 +8,7 @@
 #include "moe_decode.h"
 #include "down.hpp"
 #include "gate_up.hpp"
+#include "gate_up_grouped.hpp"
 #include "peak.hpp"
 
 namespace {
@@ -99,8 +100,72 @@ GateUpLaunch pick_gate_up(int nch, int r) {
   return nullptr;
 }
 
+// ---------------------------------------------------------------- gate/up, expert-grouped
+// converted rows take R x passes x 2 x 8 VGPRs
+constexpr bool grouped_fits(int nch, int r) { return nch * r <= 8; }
+bool grouped_allowed(int nch, int r, long long slots) {
+  return (r == 1 || r == 2 || r == 4 || r == 8) && nch >= 1 && nch <= kMaxGateUpPasses && grouped_fits(nch, r) &&
+         slots <= moe::kGroupedMaxSlots;
+}
+
+template <int NCH, int R>
+void launch_grouped_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
+                      const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
+  hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
+                     tiles);
+}
+
+template <int NCH, int R>
+GateUpLaunch grouped_fn() {
+  if constexpr (grouped_fits(NCH, R)) return launch_grouped_t<NCH, R>;
+  else return nullptr;
+}
+
+template <int NCH>
+GateUpLaunch pick_grouped_r(int r) {
+  switch (r) {
+    case 1: return grouped_fn<NCH, 1>();
+    case 2: return grouped_fn<NCH, 2>();
+    case 4: return grouped_fn<NCH, 4>();
+    case 8: return grouped_fn<NCH, 8>();
+  }
+  return nullptr;
+}
+
+GateUpLaunch pick_grouped(int nch, int r) {
+  switch (nch) {
+    case 1: return pick_grouped_r<1>(r);
+    case 2: return pick_grouped_r<2>(r);
+    case 3: return pick_grouped_r<3>(r);
+    case 4: return pick_grouped_r<4>(r);
+    case 5: return pick_grouped_r<5>(r);
+    case 6: return pick_grouped_r<6>(r);
+    case 7: return pick_grouped_r<7>(r);
+    case 8: return pick_grouped_r<8>(r);
+  }
+  return nullptr;
+}
+
+// Variant table: the per-slot kernel measured faster than the expert-grouped
+// one at every batch size and shape swept on MI355X (B = 1..64, H = 2048 and
+// 4096), so the table always takes it; the grouped kernel stays available
+// through moe_decode_gate_up_ex.
+int gate_up_default_variant(int B, int H, int I, int E, int k) {
+  (void)B; (void)H; (void)I; (void)E; (void)k;
+  return MOE_GATE_UP_PER_SLOT;
+}
+
+// two rows per wave unless the converted rows would exceed 64 VGPRs
+int grouped_default_rows(int H) {
+  const int nch = passes(H);
+  int r = 2;
+  while (r > 1 && nch * r > 4) r /= 2;
+  return r;
+}
+
 int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg, const uint8_t* wu,
-                 const uint8_t* su, void* h, int B, int H, int I, int E, int k, int rows, void* stream) {
+                 const uint8_t* su, void* h, int B, int H, int I, int E, int k, int variant, int rows, void* stream) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
   if (B == 0) return MOE_OK;
@@ -112,12 +177,26 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
       overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
     return MOE_ERR_ALIAS;
   const int nch = passes(H);
-  if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
-  if (!gate_up_allowed(nch, rows)) return MOE_ERR_ARG;
-  GateUpLaunch fn = pick_gate_up(nch, rows);
+  if (variant == 0) variant = gate_up_default_variant(B, H, I, E, k);
+  GateUpLaunch fn = nullptr;
+  long long units = 0;
+  if (variant == MOE_GATE_UP_PER_SLOT) {
+    if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
+    if (!gate_up_allowed(nch, rows)) return MOE_ERR_ARG;
+    fn = pick_gate_up(nch, rows);
+    units = (long long)B * k;
+  } else if (variant == MOE_GATE_UP_EXPERT_GROUPED) {
+    if (rows == 0) rows = grouped_default_rows(H);
+    if (!grouped_allowed(nch, rows, (long long)B * k)) return MOE_ERR_ARG;
+    fn = pick_grouped(nch, rows);
+    units = E;
+  } else {
+    return MOE_ERR_ARG;
+  }
   if (!fn) return MOE_ERR_ARG;
   const int tiles = (I + rows - 1) / rows;
-  const long long waves = (long long)tiles * B * k;
+  const long long waves = (long long)tiles * units;
+  if (waves >= (1LL << 31)) return MOE_ERR_SHAPE;
   const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
   (void)hipGetLastError();
   fn(grid, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles);
@@ -210,14 +289,14 @@ extern "C" {
 int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* w_gate, const uint8_t* s_gate,
                        const uint8_t* w_up, const uint8_t* s_up, void* h_out, int B, int H, int I, int E, int k,
                        void* stream) {
-  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, 0, stream);
+  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, 0, 0, stream);
 }
 
 int moe_decode_gate_up_ex(const void* x, const int32_t* topk_ids, const uint8_t* w_gate, const uint8_t* s_gate,
                           const uint8_t* w_up, const uint8_t* s_up, void* h_out, int B, int H, int I, int E, int k,
-                          int rows_per_wave, void* stream) {
-  if (rows_per_wave < 0) return MOE_ERR_ARG;
-  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, rows_per_wave, stream);
+                          int variant, int rows_per_wave, void* stream) {
+  if (rows_per_wave < 0 || variant < 0) return MOE_ERR_ARG;
+  return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, variant, rows_per_wave, stream);
 }
 
 int moe_decode_down(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
@@ -232,13 +311,16 @@ int moe_decode_down_ex(const void* h, const int32_t* topk_ids, const float* topk
   return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, rows_per_wave, stream);
 }
 
-int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* rows_per_wave, int* workgroups) {
+int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int* rows_per_wave, int* workgroups) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
-  if (!rows_per_wave || !workgroups) return MOE_ERR_NULL;
-  const int r = gate_up_default_rows(B, H, I, k);
+  if (!variant || !rows_per_wave || !workgroups) return MOE_ERR_NULL;
+  const int v = gate_up_default_variant(B, H, I, E, k);
+  const int r = v == MOE_GATE_UP_PER_SLOT ? gate_up_default_rows(B, H, I, k) : grouped_default_rows(H);
+  const long long units = v == MOE_GATE_UP_PER_SLOT ? (long long)B * k : (long long)E;
+  *variant = v;
   *rows_per_wave = r;
-  *workgroups = (int)((((long long)(I + r - 1) / r) * B * k + kWavesPerBlock - 1) / kWavesPerBlock);
+  *workgroups = (int)((((long long)(I + r - 1) / r) * units + kWavesPerBlock - 1) / kWavesPerBlock);
   return MOE_OK;
 }
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_error_codes_match_header():
     src = open(HEADER).read()
-    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MOE_\w+) \(?(-?\d+)\)?", src)}
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MOE_(?:OK|ERR_\w+)) \(?(-?\d+)\)?", src)}
     for name, val in codes.items():
         assert getattr(mg, name) == val, name
     for val in codes.values():
@@ -48,12 +48,12 @@ S = 0x1000000000     # spaced 64 GiB apart so only the planted overlaps overlap
 
 
 def gu(x=A, ids=A + 1 * S, wg=A + 2 * S, sg=A + 3 * S, wu=A + 4 * S, su=A + 5 * S, h=A + 6 * S,
-       B=2, H=2048, I=768, E=128, k=8, rows=None):
+       B=2, H=2048, I=768, E=128, k=8, rows=None, variant=0):
     L = mg.lib()
     args = [ctypes.c_void_p(p) for p in (x, ids, wg, sg, wu, su, h)] + [B, H, I, E, k]
     if rows is None:
         return L.moe_decode_gate_up(*args, None)
-    return L.moe_decode_gate_up_ex(*args, rows, None)
+    return L.moe_decode_gate_up_ex(*args, variant, rows, None)
 
 
 def dn(h=A, ids=A + 1 * S, tw=A + 2 * S, wd=A + 3 * S, sd=A + 4 * S, y=A + 5 * S,
@@ -112,14 +112,23 @@ def test_bad_tuning_arguments():
     assert gu(rows=3) == mg.MOE_ERR_ARG
     assert gu(rows=-1) == mg.MOE_ERR_ARG
     assert gu(rows=16) == mg.MOE_ERR_ARG
-    assert gu(H=8192, rows=4) == mg.MOE_ERR_ARG      # 4 blocks/lane x 4 rows exceeds the register budget
+    assert gu(H=8192, rows=4) == mg.MOE_ERR_ARG      # 8 passes x 4 rows exceeds the register budget
+    assert gu(rows=1, variant=3) == mg.MOE_ERR_ARG
+    assert gu(rows=1, variant=-1) == mg.MOE_ERR_ARG
+    assert gu(rows=8, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG      # 2 passes x 8 rows > 8
+    assert gu(B=129, rows=1, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG   # B*k > 1024
     assert dn(rows=5) == mg.MOE_ERR_ARG
-    assert dn(I=1536, rows=8) == mg.MOE_ERR_ARG      # 6 blocks/lane x 8 rows exceeds the register budget
+    assert dn(I=1536, rows=8) == mg.MOE_ERR_ARG      # 12 passes x 8 rows exceeds the register budget
 
 
 def test_plans():
-    r, g = mg.moe_decode_gate_up_plan(32, 2048, 768, 128, 8)
-    assert r in (1, 2, 4, 8) and g == -(-((768 + r - 1) // r) * 32 * 8 // 4)
+    for B in (1, 8, 32, 64):
+        v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
+        units = B * 8 if v == mg.MOE_GATE_UP_PER_SLOT else 128
+        assert v in (mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED)
+        assert r in (1, 2, 4, 8) and g == -(-((768 + r - 1) // r) * units // 4)
+    assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     r, g = mg.moe_decode_down_plan(32, 2048, 768, 128, 8)
     assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * 32 // 4)
     with pytest.raises(mg.MoeDecodeError):

@@ -48,12 +48,12 @@ class DevLayer:
         return (L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
 
 
-def run_gpu(D, x, ids, w, dev, rows_gu=None, rows_dn=None, stream=None):
+def run_gpu(D, x, ids, w, dev, rows_gu=None, rows_dn=None, stream=None, variant=None):
     B, k = ids.shape
     xd, idd, wdv = _t(x, dev), _t(ids, dev), _t(w, dev)
     h = torch.empty((B, k, D.I), dtype=torch.int16, device=dev)
     y = torch.empty((B, D.H), dtype=torch.int16, device=dev)
-    mg.moe_decode_gate_up(xd, idd, D.wg, D.sg, D.wu, D.su, h, stream=stream, rows_per_wave=rows_gu)
+    mg.moe_decode_gate_up(xd, idd, D.wg, D.sg, D.wu, D.su, h, stream=stream, rows_per_wave=rows_gu, variant=variant)
     mg.moe_decode_down(h, idd, wdv, D.wd, D.sd, y, stream=stream, rows_per_wave=rows_dn)
     torch.cuda.synchronize()
     return h.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16)
@@ -116,18 +116,35 @@ def small_layers(dev):
 
 @pytest.mark.parametrize("shape", SMALL, ids=[str(s) for s in SMALL])
 @pytest.mark.parametrize("rows", [None, 1, 2, 4, 8])
-def test_small_shapes_all_variants(dev, small_layers, shape, rows):
+@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+def test_small_shapes_all_variants(dev, small_layers, shape, rows, variant):
     B, H, I, E, k = shape
     D = small_layers[shape]
     # register-feasible variants only (passes of 1024 elements per lane group)
     n_gu, n_dn = -(-H // 1024), -(-(k * I) // 1024)
-    rows_gu = rows if rows is None or rows * n_gu <= 16 else None
+    cap = 16 if variant == mg.MOE_GATE_UP_PER_SLOT else 8
+    rows_gu = rows if rows is None or rows * n_gu <= cap else None
     rows_dn = rows if rows is None or n_dn * (5 * rows + 8) <= 224 else None
     x = mi.make_x(7, B, H)
     ids, w = mi.route_uniform(7, B, E, k)
-    h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn)
+    h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn, variant=variant)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
-    check(h, y, h_ref, y_ref, B, k, f"{shape} rows={rows}")
+    check(h, y, h_ref, y_ref, B, k, f"{shape} rows={rows} variant={variant}")
+
+
+@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+def test_duplicate_ids_within_a_token(dev, small_layers, variant):
+    """A token may list one expert twice; each slot is computed and summed on its own."""
+    shape = (3, 2048, 96, 16, 8)
+    B, H, I, E, k = shape
+    D = small_layers[shape]
+    x = mi.make_x(8, B, H)
+    ids, w = mi.route_uniform(8, B, E, k)
+    ids[0, 1] = ids[0, 0]
+    ids[2, :] = 5
+    h, y = run_gpu(D, x, ids, w, dev, variant=variant)
+    h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
+    check(h, y, h_ref, y_ref, B, k, f"duplicates variant={variant}")
 
 
 # --------------------------------------------------------------- full-size workloads
@@ -137,13 +154,17 @@ def s1(dev):
     return DevLayer(mi.make_layer(mi.layer_seed(1), s["H"], s["I"], s["E"]), dev)
 
 
-def _full(D, config, B, routing, dev, it=0):
+def _full(D, config, B, routing, dev, it=0, variants=(None,)):
     seed = mi.routing_seed(config, B, routing)
     x = mi.make_x(seed, B, D.H, it=it)
     ids, w = mi.make_routing(routing, seed, B, D.E, 8, it=it)
-    h, y = run_gpu(D, x, ids, w, dev)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
-    check(h, y, h_ref, y_ref, B, 8, f"config{config} B={B} {routing}")
+    for v in variants:
+        h, y = run_gpu(D, x, ids, w, dev, variant=v)
+        check(h, y, h_ref, y_ref, B, 8, f"config{config} B={B} {routing} variant={v}")
+
+
+BOTH = (None, mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED)
 
 
 def test_config1_single_layer_b1(dev, s1):
@@ -152,12 +173,12 @@ def test_config1_single_layer_b1(dev, s1):
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
 def test_config2_batch_sweep(dev, s1, B):
-    _full(s1, 2, B, "uniform", dev)
+    _full(s1, 2, B, "uniform", dev, variants=BOTH)
 
 
 @pytest.mark.parametrize("routing", ["zipf", "adversarial", "contiguous"])
 def test_config3_routing_stress(dev, s1, routing):
-    _full(s1, 3, 32, routing, dev)
+    _full(s1, 3, 32, routing, dev, variants=BOTH)
 
 
 @pytest.mark.parametrize("layer", [1, 47])
@@ -180,10 +201,11 @@ def test_config5_wide_layer_sampled_tokens(dev):
         seed = mi.routing_seed(5, B, layer=0)
         x = mi.make_x(seed, B, D.H)
         ids, w = mi.route_uniform(seed, B, D.E, 8)
-        h, y = run_gpu(D, x, ids, w, dev)
         toks = sorted({0, B // 2, B - 1})
         h_ref, y_ref = oracle.layer(x[toks], ids[toks], w[toks], *D.host())
-        check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"config5 B={B} tokens={toks}")
+        for v in BOTH:
+            h, y = run_gpu(D, x, ids, w, dev, variant=v)
+            check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"config5 B={B} tokens={toks} variant={v}")
 
 
 # --------------------------------------------------------------- properties
@@ -262,14 +284,15 @@ def test_empty_batch(dev, s1):
     torch.cuda.synchronize()
 
 
-def test_out_of_range_ids_give_nan_not_faults(dev, s1):
+@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+def test_out_of_range_ids_give_nan_not_faults(dev, s1, variant):
     B, k = 4, 8
     x = mi.make_x(88, B, s1.H)
     ids, w = mi.route_uniform(88, B, s1.E, k)
     bad = ids.copy()
     bad[1, 3] = -1
     bad[2, 0] = s1.E
-    h, y = run_gpu(s1, x, bad, w, dev)
+    h, y = run_gpu(s1, x, bad, w, dev, variant=variant)
     h_ref, y_ref = oracle.layer(x, ids, w, *s1.host())
     hv, yv = oracle.bf16_to_f64(h), oracle.bf16_to_f64(y)
     assert np.all(np.isnan(hv[1, 3])) and np.all(np.isnan(hv[2, 0]))
