@@ -128,17 +128,14 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
     }
     nan_rows |= (uint64_t)(nan_lanes != 0) << r;
   }
+  // one reduce-scatter of the R sums; output r is written by scatter_lane<R>(r)
+  const float tot = wave_reduce_scatter<R>(acc, lane);
+  int r_out = -1;
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum_row3(acc[r]);
-
-  // lanes 48..63 hold the sums; lane 48 + r writes output o0 + r
-  const int r_out = lane - kSumLane;
-  float v = acc[0];
-#pragma unroll
-  for (int r = 1; r < R; ++r) v = (r_out == r) ? acc[r] : v;
-  if (r_out >= 0 && r_out < R && o0 + r_out < H) {
+  for (int r = 0; r < R; ++r) r_out = (lane == scatter_lane<R>(r)) ? r : r_out;
+  if (r_out >= 0 && o0 + r_out < H) {
     const bool nan_out = bad_token || ((nan_rows >> r_out) & 1);
-    y[(size_t)b * H + o0 + r_out] = f32_to_bf16_rne(nan_out ? qnan() : v);
+    y[(size_t)b * H + o0 + r_out] = f32_to_bf16_rne(nan_out ? qnan() : tot);
   }
 }
 

@@ -14,8 +14,9 @@
 // straight-line: every load of the wave is issued before the first
 // arithmetic, so each wave keeps R*4 KB in flight; lanes past the end of a
 // row re-read its last chunk and contribute zero.  Loads are buffer loads:
-// scalar base, 32-bit lane offset, scalar row offset.  Per-lane partial sums
-// are reduced across the wave with DPP row operations, not LDS.
+// scalar base, 32-bit lane offset, scalar row offset.  The 2R per-lane
+// partial sums are reduced in one reduce-scatter (permlane swaps across rows,
+// DPP inside rows), not through LDS.
 //
 // Grid order: wave id = tile * (B*k) + slot, tile (neuron group) slowest, and
 // workgroups are remapped so that each XCD runs a contiguous range of tiles.
@@ -105,23 +106,23 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     }
     nan_rows |= (uint64_t)(nan_lanes != 0) << r;
   }
+  // one reduce-scatter of the 2R sums: g[r] is index r, u[r] index R + r
+  float v[2 * R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    g[r] = wave_sum_row3(g[r]);
-    u[r] = wave_sum_row3(u[r]);
+    v[r] = g[r];
+    v[R + r] = u[r];
   }
-
-  // lanes 48..63 hold the sums; lane 48 + r writes neuron n0 + r
-  const int r_out = lane - kSumLane;
-  float gv = g[0], uv = u[0];
+  const float tot = wave_reduce_scatter<2 * R>(v, lane);
+  // index R + r sits 32 lanes above index r: fetch it into the lower half
+  float lo = tot, hi = tot;
+  permlane32_swap(lo, hi);   // hi (lanes 0..31) = tot of lanes 32..63
+  int r_out = -1;
 #pragma unroll
-  for (int r = 1; r < R; ++r) {
-    gv = (r_out == r) ? g[r] : gv;
-    uv = (r_out == r) ? u[r] : uv;
-  }
-  if (r_out >= 0 && r_out < R && n0 + r_out < I) {
+  for (int r = 0; r < R; ++r) r_out = (lane == scatter_lane<2 * R>(r)) ? r : r_out;
+  if (r_out >= 0 && n0 + r_out < I) {
     const bool nan_out = bad || ((nan_rows >> r_out) & 1);
-    const float hv = nan_out ? qnan() : silu(gv) * uv;
+    const float hv = nan_out ? qnan() : silu(tot) * hi;
     h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(hv);
   }
 }
