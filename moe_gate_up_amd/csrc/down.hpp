@@ -12,10 +12,12 @@
 // (router weight x block scale) into a single multiplier per chunk, and each
 // load instruction covers whole cache lines of at most two rows.  At I=768 a
 // single row is too short for 64 lanes x 16 bytes; the 6144 concatenated
-// elements of 8 experts are 6 passes.  h[b] is loaded once per wave and
-// reused for the R outputs.  Straight-line code with buffer loads (scalar
-// base, 32-bit lane offset, scalar row offset); every load is issued before
-// the first arithmetic.
+// elements of 8 experts are 6 passes.  The 4 wavefronts of a workgroup serve
+// the same token, so h[b] (2*k*I bytes) is loaded once per workgroup into LDS,
+// a quarter by each wavefront, and read back after one barrier; it is reused
+// for the R outputs of every wavefront.  Straight-line code with buffer loads
+// (scalar base, 32-bit lane offset, scalar row offset); every global load is
+// issued before the first arithmetic.
 //
 // Grid order: tile-major in groups of 4 tiles (wave id = (group, b, tile in
 // group)), with workgroups remapped so that each XCD runs a contiguous range
@@ -36,6 +38,7 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
   const int lane = threadIdx.x & 63;
   // wave-uniform: keep the index math in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
+  // o_tiles is a multiple of 4 and the grid is exact: no wave leaves before the barrier
   if (wave >= o_tiles * B) return;
   // (H/R is a multiple of 4 because H is a multiple of 32 and R <= 8)
   const int grp = __builtin_amdgcn_readfirstlane(wave / (4 * B));   // VALU division, uniform result
@@ -51,16 +54,20 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
   const rsrc_t hr = make_rsrc(h, (uint64_t)B * k * I * 2);
   const rsrc_t idr = make_rsrc(ids, (uint64_t)B * k * 4), twr = make_rsrc(tw, (uint64_t)B * k * 4);
 
-  // h[b] does not depend on the routing: issue its loads first
+  // h[b] does not depend on the routing: issue its loads first, 16 bytes per
+  // thread and piece, workgroup-wide
+  constexpr int NLD = (NP + 1) / 2;   // 2*k*I <= NP * 2 KB = NLD pieces of 256 x 16 B
   const uint32_t hbase = (uint32_t)b * (uint32_t)n_tot * 2u;
-  uint32_t off[NP];
-  u32x4 ha[NP][2];
+  u32x4 hv[NLD];
+  uint32_t hoff[NLD];
 #pragma unroll
-  for (int c = 0; c < NP; ++c) {
-    off[c] = (uint32_t)min(1024 * c + 16 * lane, n_tot - 16);   // clamped duplicates fold with weight 0
-    ha[c][0] = bload16(hr, off[c] * 2u, hbase);
-    ha[c][1] = bload16(hr, off[c] * 2u + 16u, hbase);
+  for (int i = 0; i < NLD; ++i) {
+    hoff[i] = (uint32_t)min(4096 * i + 16 * (int)threadIdx.x, 2 * n_tot - 16);   // clamped: duplicate, same value
+    hv[i] = bload16(hr, hoff[i], hbase);
   }
+  uint32_t off[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) off[c] = (uint32_t)min(1024 * c + 16 * lane, n_tot - 16);   // clamped duplicates fold with weight 0
 
   // slot j = off / I of each chunk: its expert, router weight and row offsets.
   // One division for pass 0; later passes step by 1024 = step_j * I + step_w.
@@ -114,20 +121,31 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
 
   // keep every load above this point: all of the wave's memory traffic is in flight at once
   __builtin_amdgcn_sched_barrier(0);
+  extern __shared__ __attribute__((aligned(16))) uint8_t hs[];   // h[b], 2*k*I bytes
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(hs + hoff[i]) = hv[i];
+  __syncthreads();
 
   float acc[R];
-  uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code among output r's rows
+  uint64_t nan_lanes[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     acc[r] = 0.0f;
-    uint64_t nan_lanes = 0;
-#pragma unroll
-    for (int c = 0; c < NP; ++c) {
-      acc[r] = fmaf(apply_e8m0(chunk_dot(w[r][c], ha[c], 0.0f), sc[r][c], bias[c]), fold[c], acc[r]);
-      nan_lanes |= nan_scale_lanes(sc[r][c]);
-    }
-    nan_rows |= (uint64_t)(nan_lanes != 0) << r;
+    nan_lanes[r] = 0;
   }
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    const u32x4* hp = reinterpret_cast<const u32x4*>(hs + off[c] * 2u);
+    const u32x4 ha[2] = {hp[0], hp[1]};   // this lane's 16 elements of h[b], shared by the R rows
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = fmaf(apply_e8m0(chunk_dot(w[r][c], ha, 0.0f), sc[r][c], bias[c]), fold[c], acc[r]);
+      nan_lanes[r] |= nan_scale_lanes(sc[r][c]);
+    }
+  }
+  uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code among output r's rows
+#pragma unroll
+  for (int r = 0; r < R; ++r) nan_rows |= (uint64_t)(nan_lanes[r] != 0) << r;
   // one reduce-scatter of the R sums; output r is written by scatter_lane<R>(r)
   const float tot = wave_reduce_scatter<R>(acc, lane);
   int r_out = -1;

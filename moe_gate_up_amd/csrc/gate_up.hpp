@@ -10,7 +10,11 @@
 // wave covers eight whole 128-byte cache lines (the contiguous access the
 // pages' copy-kernel peak is measured with).  Two neighbouring lanes share
 // the E8M0 scale of their 32-element block.  The lane's slice of x[b] is
-// loaded once and reused for the R gate rows and R up rows.  The code is
+// loaded once and reused for the R gate rows and R up rows.  When k is a
+// multiple of 4 (XL), the 4 wavefronts of a workgroup are 4 slots of the same
+// token: each loads a quarter of x[b] into LDS and all four read it back
+// after one barrier, which takes 3/4 of the activation loads off the vector
+// memory pipeline that the weight stream needs.  The code is
 // straight-line: every load of the wave is issued before the first
 // arithmetic, so each wave keeps R*4 KB in flight; lanes past the end of a
 // row re-read its last chunk and contribute zero.  Loads are buffer loads:
@@ -28,7 +32,7 @@
 
 namespace moe {
 
-template <int NCH, int R>
+template <int NCH, int R, bool XL>
 __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
@@ -38,6 +42,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   // wave-uniform: keep the index math in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
   const int slots = B * k;
+  // With XL the grid is exact (B*k and so n_tiles*B*k are multiples of 4), so
+  // no wave of a workgroup leaves before the barrier.
   if (wave >= n_tiles * slots) return;
   // integer division runs on the VALU; readfirstlane returns the (uniform) results to SGPRs
   const int tile = __builtin_amdgcn_readfirstlane(wave / slots);
@@ -67,10 +73,21 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
 
   const uint32_t xoff = (uint32_t)b * (uint32_t)H * 2u;
   u32x4 xa[NCH][2];
+  constexpr int NX = (NCH + 1) / 2;   // XL: 16-byte pieces of x[b] per thread (256 threads x 16 B per piece)
+  u32x4 xv[NX];
+  uint32_t xo[NX];
+  if constexpr (XL) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    xa[c][0] = bload16(xr, off[c] * 2u, xoff);
-    xa[c][1] = bload16(xr, off[c] * 2u + 16u, xoff);
+    for (int i = 0; i < NX; ++i) {
+      xo[i] = (uint32_t)min(4096 * i + 16 * (int)threadIdx.x, 2 * H - 16);   // clamped: duplicate, same value
+      xv[i] = bload16(xr, xo[i], xoff);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      xa[c][0] = bload16(xr, off[c] * 2u, xoff);
+      xa[c][1] = bload16(xr, off[c] * 2u + 16u, xoff);
+    }
   }
 
   u32x4 gw[R][NCH], uw[R][NCH];
@@ -90,6 +107,18 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
 
   // keep every load above this point: all of the wave's memory traffic is in flight at once
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // x[b], 2H bytes
+#pragma unroll
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(xs + xo[i]) = xv[i];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(xs + off[c] * 2u);
+      xa[c][0] = p[0];
+      xa[c][1] = p[1];
+    }
+  }
 
   float g[R], u[R];
   uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code in row r

@@ -58,12 +58,19 @@ int gate_up_default_rows(int B, int H, int I, int k) {
   return r;
 }
 
+// k % 4 == 0: the 4 wavefronts of a workgroup serve one token and share x[b] through LDS
 template <int NCH, int R>
 void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
                       const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
-  hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
-                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
-                     tiles);
+  static_assert(kWavesPerBlock == 4, "x sharing assumes 4 slots per workgroup");
+  if (k % 4 == 0)
+    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, true>), grid, dim3(64 * kWavesPerBlock),
+                       (unsigned)(2 * H), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu, su,
+                       static_cast<uint16_t*>(h), B, H, I, E, k, tiles);
+  else
+    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, false>), grid, dim3(64 * kWavesPerBlock), 0, st,
+                       static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
+                       tiles);
 }
 
 using GateUpLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
@@ -222,7 +229,8 @@ int down_default_rows(int B, int H, int I, int k) {
 template <int NP, int R>
 void launch_down_t(dim3 grid, hipStream_t st, const void* h, const int32_t* ids, const float* tw, const uint8_t* wd,
                    const uint8_t* sd, void* y, int B, int H, int I, int E, int k, int tiles) {
-  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
+  // dynamic LDS: h[b] of the workgroup's token, 2*k*I <= 32 KB
+  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), grid, dim3(64 * kWavesPerBlock), (unsigned)(2 * k * I), st,
                      static_cast<const uint16_t*>(h), ids, tw, wd, sd, static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
 }
 
