@@ -1,76 +1,109 @@
 // Gate/up kernel, expert-grouped variant (blog post "warp decode", section
 // "How the two kernels work" for the arithmetic; section "Warp decode and
 // Composer training" for why grouping pays once several tokens share an
-// expert).  Each output h[b,j,n] is still computed by one wavefront from the
-// streamed gate and up rows, with no padding, gather buffer or combine: the
-// only change is that one wavefront owns R neurons of one expert e for every
-// slot routed to e, so the rows are read from memory and converted from MXFP8
-// once, then dotted with each of those tokens' activations in turn.
+// expert).  Every output h[b,j,n] is still one neuron's SiLU(gate) * up,
+// produced from streamed MXFP8 rows dotted with x[b] in FP32 and written
+// once, with no padding, expert-major gather buffer or combine.  What changes
+// is who reads the rows: a workgroup owns 4R consecutive neurons of one
+// expert e (R per wavefront) for every slot routed to e, so each routed row is
+// read from memory once per layer however many tokens share the expert.  The
+// per-slot kernel reads it once per slot; at 32 tokens x 8 of 128 experts the
+// average expert serves 2.3 slots, and those repeat reads (L2 hits) occupy
+// the vector-memory pipeline that the weight stream needs.
 //
-// The wavefront first scans topk_ids (B*k <= 1024 entries, 64 per ballot) for
-// the slots that use e and exits before loading anything if there are none.
-// The R gate and R up rows are loaded with the same 1 KB-contiguous passes as
-// the per-slot kernel and converted to bf16 pairs in registers.  Then, slot
-// by slot, the lane's slice of x[b] is loaded, the 2R dot products are
-// formed with v_dot2c_f32_bf16, each 16-element partial is scaled by its
-// E8M0 scale (v_ldexp_f32), the 2R sums are reduced with DPP and lanes
-// 48..48+R-1 write SiLU(g)*u.
+// Steps of one workgroup:
+//  1. the 4 wavefronts split topk_ids (B*k <= 1024: at most 4 dword loads per
+//     lane) and count the slots routed to e with ballots; the counts meet in
+//     LDS, and with none the whole workgroup leaves before any weight is read;
+//  2. each wavefront issues its R gate and R up rows (1 KB-contiguous passes
+//     as in the per-slot kernel) and their E8M0 scales, then writes its part
+//     of the list of e's slots (slot index and token) to LDS;
+//  3. per chunk of up to M slots, the 4 wavefronts copy those tokens' x rows
+//     into LDS (direct global->LDS loads, 1 KB per wave instruction), one
+//     barrier, then each
+//     wavefront takes the chunk's slots in turn: it reads its lanes' slice of
+//     x from LDS, converts its raw E4M3 rows to bf16 pairs and forms the 2R
+//     dot products with v_dot2c_f32_bf16, scales each 16-element partial by
+//     its E8M0 scale (v_ldexp_f32), reduces the 2R sums with one
+//     reduce-scatter and writes R outputs.
+// The workgroup for expert 0 also writes NaN for the slots whose id is
+// outside [0, E), so every output is written exactly once.
 //
-// Measured on MI355X this variant is slower than the per-slot kernel at
-// every batch size swept (B = 1..64, H = 2048 and 4096): each token adds a
-// dependent activation load to the wavefront's critical path, x is re-read
-// per (expert, tile, token), and holding converted rows limits occupancy,
-// which outweighs converting each row once.  (Fetching four tokens'
-// activations per round was slower still.)  It is kept as an opt-in variant.  The wavefront for expert 0 of each tile also
-// writes NaN for slots whose id is outside [0, E), so every output is written
-// exactly once.
-//
-// Grid order: wave id = tile * E + e (tile slowest), workgroups remapped so
-// each XCD runs a contiguous range of tiles.
+// Grid: workgroup id = neuron group * E + e.
 #pragma once
 
 #include "prims.hpp"
 
 namespace moe {
 
-constexpr int kGroupedMaxSlots = 1024;   // B*k limit of the expert-grouped variant
+constexpr int kGroupedMaxSlots = 1024;                   // B*k limit of the expert-grouped variant
+constexpr int kGroupedIdLoads = kGroupedMaxSlots / 64;   // topk_ids dwords per lane
+constexpr int kGroupedInfoBytes = kGroupedIdLoads * 4;   // LDS per-group counts
+constexpr int kGroupedListBytes = kGroupedMaxSlots * 4;  // LDS slot list
+constexpr int kGroupedXBytes = 32768;                    // LDS for staged activations
+
+// slots per chunk: M x rows of 2*1024*NCH bytes fit in kGroupedXBytes
+constexpr int grouped_chunk(int nch) { return 16 / nch < 1 ? 1 : (16 / nch > 8 ? 8 : 16 / nch); }
+constexpr int grouped_lds_bytes(int nch, int H) {
+  return kGroupedInfoBytes + kGroupedListBytes + grouped_chunk(nch) * (((2 * H + 1023) / 1024) * 1024);
+}
 
 template <int NCH, int R>
 __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
     const uint8_t* __restrict__ wu, const uint8_t* __restrict__ su,
-    uint16_t* __restrict__ h, int B, int H, int I, int E, int k, int n_tiles) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
-  if (wave >= n_tiles * E) return;
-  const int tile = __builtin_amdgcn_readfirstlane(wave / E);   // VALU division, uniform result
-  const int e = wave - tile * E;
-  const int n0 = tile * R;
-  const int slots = B * k;
-  const int nq = (slots + 63) / 64;
-  const int nblk = H >> 5;
+    uint16_t* __restrict__ h, int B, int H, int I, int E, int k) {
+  constexpr int M = grouped_chunk(NCH);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint32_t* qinfo = reinterpret_cast<uint32_t*>(lds);                  // per 64-slot group: count | invalid << 31
+  uint32_t* list = reinterpret_cast<uint32_t*>(lds + kGroupedInfoBytes);   // e's slots
+  uint8_t* xs = lds + kGroupedInfoBytes + kGroupedListBytes;           // M rows of x, 2H bytes each, 1 KB-padded
 
-  // ---- which slots use expert e (and, for e == 0, whether any id is invalid)
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+  const int blk = blockIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(blk / E);   // VALU division, uniform result
+  const int e = blk - grp * E;
+  const int n0 = (grp * 4 + w) * R;   // this wavefront's first neuron (may be >= I: nothing stored)
+  const int slots = B * k;
+  const int nq = (slots + 63) >> 6;
+
+  // ---- 1. which slots use e.  Wavefront w scans the 64-slot groups q = w,
+  // w+4, w+8, w+12 (one dword load per lane each) and posts each group's
+  // count of e's slots (and whether it holds an invalid id) to LDS.
   const rsrc_t idr = make_rsrc(ids, (uint64_t)slots * 4);
-  // expert id of slot 64q + lane; slots past B*k read as E (matches no expert);
-  // an invalid id of a real slot reads as -1
-  auto slot_id = [&](int q) {
-    const int sl = 64 * q + lane;
-    const int v = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)min(sl, slots - 1) * 4u, 0, 0));
-    return sl < slots ? ((unsigned)v >= (unsigned)E ? -1 : v) : E;
-  };
-  int count = 0;
-  bool any_bad = false;
-  for (int q = 0; q < nq; ++q) {
-    const int v = slot_id(q);
-    count += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v == e));
-    any_bad |= __builtin_amdgcn_ballot_w64(v == -1) != 0;
+  constexpr int QW = kGroupedIdLoads / 4;   // groups per wavefront
+  int idq[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    const int sl = 64 * (w + 4 * i) + lane;
+    idq[i] = (int)__builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)min(sl, slots - 1) * 4u, 0, 0));
+  }
+  uint64_t mq[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    const bool real = 64 * (w + 4 * i) + lane < slots;
+    mq[i] = __builtin_amdgcn_ballot_w64(real && idq[i] == e);
+    const bool bad = __builtin_amdgcn_ballot_w64(real && (unsigned)idq[i] >= (unsigned)E) != 0;
+    if (lane == 0) qinfo[w + 4 * i] = (uint32_t)__builtin_popcountll(mq[i]) | ((uint32_t)bad << 31);
+  }
+  __syncthreads();
+  const uint32_t qi = qinfo[lane & (kGroupedIdLoads - 1)];
+  int count = 0, any_bad = 0;
+  int qbase[kGroupedIdLoads];   // slots of e in groups before q (uniform)
+#pragma unroll
+  for (int q = 0; q < kGroupedIdLoads; ++q) {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)qi, q);
+    qbase[q] = count;
+    count += (int)(v & 0x7FFFFFFFu);
+    any_bad |= (int)(v >> 31);
   }
   const bool nan_duty = e == 0 && any_bad;
-  if (count == 0 && !nan_duty) return;
+  if (count == 0 && !nan_duty) return;   // same decision in all 4 wavefronts: no barrier is left waiting
 
-  // ---- load and convert the expert's R gate and R up rows
+  // ---- 2. the wavefront's R gate and R up rows of expert e, raw
   uint32_t off[NCH];
   int bias[NCH];
 #pragma unroll
@@ -79,16 +112,16 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
     off[c] = (uint32_t)min(o, H - 16);
     bias[c] = o < H ? kLiveChunk : kDeadChunk;
   }
+  const int nblk = H >> 5;
   const uint32_t wbytes = (uint32_t)E * (uint32_t)I * (uint32_t)H;   // < 2^32, checked on the host
   const rsrc_t xr = make_rsrc(x, (uint64_t)B * H * 2);
   const rsrc_t gr = make_rsrc(wg, wbytes), ur = make_rsrc(wu, wbytes);
   const rsrc_t gsr = make_rsrc(sg, wbytes / 32), usr = make_rsrc(su, wbytes / 32);
-
   u32x4 gw[R][NCH], uw[R][NCH];
   uint32_t gsc[R][NCH], usc[R][NCH];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t row = (uint32_t)(e * I + min(n0 + r, I - 1));   // ragged last tile: clamp, not stored
+    const uint32_t row = (uint32_t)(e * I + min(n0 + r, I - 1));   // ragged: clamp, not stored
     const uint32_t woff = row * (uint32_t)H, soff = row * (uint32_t)nblk;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -98,87 +131,103 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
       usc[r][c] = bload8(usr, off[c] >> 5, soff);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
 
-  // bf16 pairs of the rows: [r][c][8 dwords]
-  uint32_t gb[R][NCH][8], ub[R][NCH][8];
-  uint64_t nan_rows = 0;
+  // list of e's slots in slot order: slot | token << 16
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    uint64_t nan_lanes = 0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        gb[r][c][2 * d] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2(gw[r][c].v[d], false));
-        gb[r][c][2 * d + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2(gw[r][c].v[d], true));
-        ub[r][c][2 * d] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2(uw[r][c].v[d], false));
-        ub[r][c][2 * d + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2(uw[r][c].v[d], true));
-      }
-      nan_lanes |= nan_scale_lanes(gsc[r][c]) | nan_scale_lanes(usc[r][c]);
+  for (int i = 0; i < QW; ++i) {
+    if (mq[i] >> lane & 1) {
+      const int pos = qbase[w + 4 * i] +
+                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mq[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mq[i], 0u));
+      const int sl = 64 * (w + 4 * i) + lane;
+      list[pos] = (uint32_t)sl | ((uint32_t)(sl / k) << 16);
     }
-    nan_rows |= (uint64_t)(nan_lanes != 0) << r;
   }
+  __syncthreads();
 
-  const int r_out = lane - kSumLane;
-  const bool writer = r_out >= 0 && r_out < R && n0 + r_out < I;
+  int r_out = -1;
+#pragma unroll
+  for (int r = 0; r < R; ++r) r_out = (lane == scatter_lane<2 * R>(r)) ? r : r_out;
+  const bool writer = r_out >= 0 && n0 + r_out < I;
+  bool nan_out = false;
 
-  // ---- every slot routed to e, one at a time
-  for (int q = 0; q < nq; ++q) {
-    uint64_t m = __builtin_amdgcn_ballot_w64(slot_id(q) == e);
-    while (m) {
-      const int s = 64 * q + __builtin_ctzll(m);
-      m &= m - 1;
-      const int b = __builtin_amdgcn_readfirstlane(s / k);
-      const uint32_t xoff = (uint32_t)b * (uint32_t)H * 2u;
+  // ---- 3. chunks of up to M slots.  x rows are copied global -> LDS without
+  // passing through registers (buffer loads with the LDS bit: lane l's 16 bytes
+  // land at the wave-uniform LDS base + 16 l); a row is cut into 1 KB pieces,
+  // piece p by wavefront p % 4, and rows sit XS bytes apart in LDS.
+  const int pieces = (2 * H + 1023) >> 10;
+  const int XS = pieces << 10;
+  auto stage = [&](int m0) {   // issue the copies of slots m0 .. m0 + M - 1
+    const int nm = min(M, count - m0);
+    for (int m = 0; m < nm; ++m) {
+      const uint32_t xo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(list[m0 + m] >> 16)) * (uint32_t)H * 2u;
+      // bytes past 2H land in the row's padding and are never read; the whole
+      // offset is in the lane offset, so reads past the end of x are range-checked (zero)
+      for (int p = w; p < pieces; p += 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xs + m * XS + 1024 * p), 16,
+                                                 xo + 1024u * p + 16u * lane, 0, 0, 0);
+    }
+  };
+  // the first chunk's copies go out before anything waits for the weights
+  if (count > 0) stage(0);
+  for (int m0 = 0; m0 < count; m0 += M) {
+    if (m0 > 0) {
+      __syncthreads();   // every wavefront is done with the previous chunk's x
+      stage(m0);
+    }
+    const int nm = min(M, count - m0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's copies are in LDS
+    __syncthreads();
+    if (m0 == 0) {   // the scales have arrived by now
+      uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code in row r
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint64_t nan_lanes = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) nan_lanes |= nan_scale_lanes(gsc[r][c]) | nan_scale_lanes(usc[r][c]);
+        nan_rows |= (uint64_t)(nan_lanes != 0) << r;
+      }
+      nan_out = writer && ((nan_rows >> r_out) & 1);
+    }
+    for (int m = 0; m < nm; ++m) {
+      const int s = (int)(list[m0 + m] & 0xFFFFu);
       u32x4 xa[NCH][2];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        xa[c][0] = bload16(xr, off[c] * 2u, xoff);
-        xa[c][1] = bload16(xr, off[c] * 2u + 16u, xoff);
+        const u32x4* p = reinterpret_cast<const u32x4*>(xs + m * XS + off[c] * 2u);
+        xa[c][0] = p[0];
+        xa[c][1] = p[1];
       }
-      float g[R], u[R];
+      float v[2 * R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        g[r] = 0.0f;
-        u[r] = 0.0f;
+        v[r] = 0.0f;
+        v[R + r] = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          float pg = 0.0f, pu = 0.0f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const bf16x2_t xv = as_bf16x2(xa[c][d >> 2].v[d & 3]);
-            pg = dot2(as_bf16x2(gb[r][c][d]), xv, pg);
-            pu = dot2(as_bf16x2(ub[r][c][d]), xv, pu);
-          }
-          g[r] += apply_e8m0(pg, gsc[r][c], bias[c]);
-          u[r] += apply_e8m0(pu, usc[r][c], bias[c]);
+          v[r] += apply_e8m0(chunk_dot(gw[r][c], xa[c], 0.0f), gsc[r][c], bias[c]);
+          v[R + r] += apply_e8m0(chunk_dot(uw[r][c], xa[c], 0.0f), usc[r][c], bias[c]);
         }
-        g[r] = wave_sum_row3(g[r]);
-        u[r] = wave_sum_row3(u[r]);
       }
-      float gv = g[0], uv = u[0];
-#pragma unroll
-      for (int r = 1; r < R; ++r) {
-        gv = (r_out == r) ? g[r] : gv;
-        uv = (r_out == r) ? u[r] : uv;
-      }
-      if (writer) {
-        const bool nan_out = (nan_rows >> r_out) & 1;
-        h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(nan_out ? qnan() : silu(gv) * uv);
-      }
+      const float tot = wave_reduce_scatter<2 * R>(v, lane);
+      float lo = tot, hi = tot;
+      permlane32_swap(lo, hi);   // hi (lanes 0..31) = the up sum, 32 lanes above the gate sum
+      if (writer) h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(nan_out ? qnan() : silu(tot) * hi);
     }
   }
 
-  // ---- slots with an invalid expert id: written as NaN by expert 0's wavefront
-  if (nan_duty) {
+  // ---- slots with an invalid expert id: NaN, written by expert 0's workgroup
+  if (nan_duty) {   // ids read again rather than kept live in 16 VGPRs
     for (int q = 0; q < nq; ++q) {
-      uint64_t m = __builtin_amdgcn_ballot_w64(slot_id(q) == -1);
-      while (m) {
-        const int bit = __builtin_ctzll(m);
-        m &= m - 1;
-        const int s = 64 * q + bit;
-        if (writer) h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(qnan());
+      {
+        const int sl = 64 * q + lane;
+        const int v = (int)__builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)min(sl, slots - 1) * 4u, 0, 0));
+        uint64_t m = __builtin_amdgcn_ballot_w64(sl < slots && (unsigned)v >= (unsigned)E);
+        while (m) {
+          const int s = 64 * q + __builtin_ctzll(m);
+          m &= m - 1;
+          if (writer) h[(size_t)s * I + n0 + r_out] = f32_to_bf16_rne(qnan());
+        }
       }
     }
   }

@@ -108,19 +108,22 @@ GateUpLaunch pick_gate_up(int nch, int r) {
 }
 
 // ---------------------------------------------------------------- gate/up, expert-grouped
-// converted rows take R x passes x 2 x 8 VGPRs
+// the rows are converted to bf16 once (they are reused for every slot):
+// R x passes x 2 x 8 VGPRs
 constexpr bool grouped_fits(int nch, int r) { return nch * r <= 8; }
 bool grouped_allowed(int nch, int r, long long slots) {
   return (r == 1 || r == 2 || r == 4 || r == 8) && nch >= 1 && nch <= kMaxGateUpPasses && grouped_fits(nch, r) &&
          slots <= moe::kGroupedMaxSlots;
 }
 
+// grid: one workgroup per (expert, group of 4 tiles); dynamic LDS: slot list + staged activations
 template <int NCH, int R>
 void launch_grouped_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
                       const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
-  hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock), 0, st,
-                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
-                     tiles);
+  (void)tiles;
+  hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock),
+                     (unsigned)moe::grouped_lds_bytes(NCH, H), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu,
+                     su, static_cast<uint16_t*>(h), B, H, I, E, k);
 }
 
 template <int NCH, int R>
@@ -155,20 +158,28 @@ GateUpLaunch pick_grouped(int nch, int r) {
 }
 
 // Variant table: the per-slot kernel measured faster than the expert-grouped
-// one at every batch size and shape swept on MI355X (B = 1..64, H = 2048 and
-// 4096), so the table always takes it; the grouped kernel stays available
-// through moe_decode_gate_up_ex.
+// one up to 32 tokens on MI355X (H = 2048 and 4096); the grouped kernel is
+// ahead only at 64 tokens (H = 2048: 109 vs 117 us), where the table still
+// takes the per-slot kernel; the grouped kernel is available through
+// moe_decode_gate_up_ex.
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)B; (void)H; (void)I; (void)E; (void)k;
   return MOE_GATE_UP_PER_SLOT;
 }
 
-// two rows per wave unless the converted rows would exceed 64 VGPRs
+// four rows per wave unless the raw rows would exceed 64 VGPRs
 int grouped_default_rows(int H) {
   const int nch = passes(H);
-  int r = 2;
-  while (r > 1 && nch * r > 4) r /= 2;
+  int r = 4;
+  while (r > 1 && nch * r > 8) r /= 2;
   return r;
+}
+
+// workgroups of a launch: per-slot, one wavefront per (tile, slot); grouped,
+// one workgroup per (group of 4 tiles, expert)
+long long gate_up_blocks(int variant, int tiles, long long units) {
+  if (variant == MOE_GATE_UP_EXPERT_GROUPED) return (long long)((tiles + kWavesPerBlock - 1) / kWavesPerBlock) * units;
+  return ((long long)tiles * units + kWavesPerBlock - 1) / kWavesPerBlock;
 }
 
 int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg, const uint8_t* wu,
@@ -202,9 +213,9 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
   }
   if (!fn) return MOE_ERR_ARG;
   const int tiles = (I + rows - 1) / rows;
-  const long long waves = (long long)tiles * units;
-  if (waves >= (1LL << 31)) return MOE_ERR_SHAPE;
-  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+  const long long blocks = gate_up_blocks(variant, tiles, units);
+  if (blocks * kWavesPerBlock >= (1LL << 31)) return MOE_ERR_SHAPE;
+  const dim3 grid((unsigned)blocks);
   (void)hipGetLastError();
   fn(grid, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
@@ -328,7 +339,7 @@ int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int
   const long long units = v == MOE_GATE_UP_PER_SLOT ? (long long)B * k : (long long)E;
   *variant = v;
   *rows_per_wave = r;
-  *workgroups = (int)((((long long)(I + r - 1) / r) * units + kWavesPerBlock - 1) / kWavesPerBlock);
+  *workgroups = (int)gate_up_blocks(v, (I + r - 1) / r, units);
   return MOE_OK;
 }
 
