@@ -64,7 +64,7 @@ def layer_bytes(ids: np.ndarray, H: int, I: int, k: int) -> dict:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gate_up.hpp", "down.hpp", "prims.hpp", "moe_decode.hip"):
+    for f in ("gate_up.hpp", "gate_up_grouped.hpp", "down.hpp", "prims.hpp", "moe_decode.hip"):
         h.update(open(os.path.join(ROOT, "moe_gate_up_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -333,9 +333,11 @@ def main():
         log(f"cpu oracle: {cpu['value']} GB/s on {cores} threads ({spent / n * 1e3:.1f} ms/layer)")
 
     traffic = measured_traffic("gate_up")
+    gu_variant = mg.moe_decode_gate_up_plan(B, H, I, E, k)[0]
     roof = {
         "bound": "hbm",
-        "kernel": "moe_gate_up_3d_batched_w64",
+        "kernel": "moe_gate_up_expert_grouped_w64" if gu_variant == mg.MOE_GATE_UP_EXPERT_GROUPED
+        else "moe_gate_up_3d_batched_w64",
         "achieved": round(kern["gate_up_GBps"], 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",

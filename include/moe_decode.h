@@ -98,13 +98,15 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *   MOE_GATE_UP_PER_SLOT: one wavefront per (R neurons, token slot) -- the
  *     blog post's organisation, one output set per warp ("How the two kernels
  *     work").  Best while few tokens share an expert.
- *   MOE_GATE_UP_EXPERT_GROUPED: one wavefront per (R neurons, expert); it
- *     finds the slots routed to its expert in topk_ids, reads and converts
- *     the expert's rows once and produces h for every such slot.  Same
- *     outputs; best once the batch routes several tokens to each expert.
- *     Requires B*k <= 1024.
- * The plain call uses MOE_GATE_UP_PER_SLOT, the faster of the two in every
- * measured configuration. */
+ *   MOE_GATE_UP_EXPERT_GROUPED: the slots are sorted by expert on the device
+ *     (inside the kernel, in LDS) and one wavefront takes R neurons of one
+ *     routed expert for every slot routed to it, reading and converting the
+ *     expert's rows once (section "Warp decode and Composer training": the
+ *     regime where several tokens share an expert).  Same outputs; requires
+ *     B*k <= 1024 and E <= 1024.
+ * The plain call takes the grouped variant once B*k >= 2E (an average of two
+ * or more slots per expert) and the limits allow it, else the per-slot one:
+ * the faster of the two in each measured configuration. */
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
 
@@ -115,7 +117,8 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  * neurons (gate/up) or output dimensions (down) one 64-lane wavefront owns;
  * 0 selects the table's choice.  Combinations beyond the register budget
  * (rows x passes of 1024 elements: <= 16 per-slot, <= 8 grouped; down:
- * passes x (5 rows + 8) <= 224) and unknown variants return MOE_ERR_ARG. */
+ * passes x (5 rows + 8) <= 224), the grouped variant beyond its limits and
+ * unknown variants return MOE_ERR_ARG. */
 int moe_decode_gate_up_ex(const void *x, const int32_t *topk_ids,
                           const uint8_t *w_gate, const uint8_t *s_gate,
                           const uint8_t *w_up, const uint8_t *s_up,

@@ -58,11 +58,20 @@ int gate_up_default_rows(int B, int H, int I, int k) {
   return r;
 }
 
-// k % 4 == 0: the 4 wavefronts of a workgroup serve one token and share x[b] through LDS
+// Every gate/up launcher returns its number of workgroups and launches only
+// when `go` is set (the plan query calls it with go = false).
+//
+// Per-slot grid: one wavefront per (tile of R neurons, slot).  k % 4 == 0:
+// the 4 wavefronts of a workgroup serve one token and share x[b] through LDS.
 template <int NCH, int R>
-void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
-                      const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
+long long launch_gate_up_t(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
+                           const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
+                           int k) {
   static_assert(kWavesPerBlock == 4, "x sharing assumes 4 slots per workgroup");
+  const int tiles = (I + R - 1) / R;
+  const long long blocks = ((long long)tiles * B * k + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (!go || blocks * kWavesPerBlock >= (1LL << 31)) return blocks;
+  const dim3 grid((unsigned)blocks);
   if (k % 4 == 0)
     hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, true>), grid, dim3(64 * kWavesPerBlock),
                        (unsigned)(2 * H), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu, su,
@@ -71,10 +80,11 @@ void launch_gate_up_t(dim3 grid, hipStream_t st, const void* x, const int32_t* i
     hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, false>), grid, dim3(64 * kWavesPerBlock), 0, st,
                        static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
                        tiles);
+  return blocks;
 }
 
-using GateUpLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
-                              const uint8_t*, const uint8_t*, void*, int, int, int, int, int, int);
+using GateUpLaunch = long long (*)(bool, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
+                                   const uint8_t*, const uint8_t*, void*, int, int, int, int, int);
 
 template <int NCH, int R>
 GateUpLaunch gate_up_fn() {
@@ -111,19 +121,31 @@ GateUpLaunch pick_gate_up(int nch, int r) {
 // the rows are converted to bf16 once (they are reused for every slot):
 // R x passes x 2 x 8 VGPRs
 constexpr bool grouped_fits(int nch, int r) { return nch * r <= 8; }
-bool grouped_allowed(int nch, int r, long long slots) {
+bool grouped_allowed(int nch, int r, long long slots, int E) {
   return (r == 1 || r == 2 || r == 4 || r == 8) && nch >= 1 && nch <= kMaxGateUpPasses && grouped_fits(nch, r) &&
-         slots <= moe::kGroupedMaxSlots;
+         slots <= moe::kGroupedMaxSlots && E <= moe::kGroupedMaxExperts;
 }
 
-// grid: one workgroup per (expert, group of 4 tiles); dynamic LDS: slot list + staged activations
+// Persistent grid of at most 2048 workgroups (8 per CU of MI355X's 256;
+// 1024 to 2560 measured within 4 %) and never more than the largest possible
+// number of work items; dynamic LDS: per-expert counters, sorted slots and
+// staged activations.
+#ifndef MOE_GROUPED_BLOCKS
+#define MOE_GROUPED_BLOCKS 2048
+#endif
+constexpr long long kGroupedBlocks = MOE_GROUPED_BLOCKS;
 template <int NCH, int R>
-void launch_grouped_t(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg,
-                      const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E, int k, int tiles) {
-  (void)tiles;
-  hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), grid, dim3(64 * kWavesPerBlock),
-                     (unsigned)moe::grouped_lds_bytes(NCH, H), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu,
-                     su, static_cast<uint16_t*>(h), B, H, I, E, k);
+long long launch_grouped_t(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
+                           const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
+                           int k) {
+  const long long slots = (long long)B * k;
+  const long long items_max = (E < slots ? E : slots) * (long long)((I + 4 * R - 1) / (4 * R));
+  const long long blocks = items_max < kGroupedBlocks ? items_max : kGroupedBlocks;
+  if (!go) return blocks;
+  hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+                     (unsigned)moe::grouped_lds_bytes(E, (int)slots, H), st, static_cast<const uint16_t*>(x), ids, wg,
+                     sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k);
+  return blocks;
 }
 
 template <int NCH, int R>
@@ -157,29 +179,40 @@ GateUpLaunch pick_grouped(int nch, int r) {
   return nullptr;
 }
 
-// Variant table: the per-slot kernel measured faster than the expert-grouped
-// one up to 32 tokens on MI355X (H = 2048 and 4096); the grouped kernel is
-// ahead only at 64 tokens (H = 2048: 109 vs 117 us), where the table still
-// takes the per-slot kernel; the grouped kernel is available through
-// moe_decode_gate_up_ex.
+// Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
+// experts, top-8, uniform routing).  While the average routed expert serves
+// few slots, the per-slot kernel wins: it needs no sort and its grid has no
+// per-workgroup setup (16 tokens, H = 2048: 47.8 vs 52.8 us).  From two slots
+// per expert on (B*k >= 2E) the expert-grouped kernel reads each routed row
+// once and wins (32 tokens: 71.5 vs 77.5 us at H = 2048, 268 vs 300 us at
+// H = 4096; 64 tokens: 95 vs 117 and 374 vs 445 us).
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
-  (void)B; (void)H; (void)I; (void)E; (void)k;
+  (void)I;
+  const long long slots = (long long)B * k;
+  if (slots >= 2LL * E && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;
 }
 
-// four rows per wave unless the raw rows would exceed 64 VGPRs
+// 4 rows per wave for one pass of 1024 elements, 2 for two, 1 beyond: the
+// rows, converted to bf16 once, stay within 64 VGPRs (same sweep)
 int grouped_default_rows(int H) {
   const int nch = passes(H);
-  int r = 4;
-  while (r > 1 && nch * r > 8) r /= 2;
-  return r;
+  return nch <= 1 ? 4 : (nch == 2 ? 2 : 1);
 }
 
-// workgroups of a launch: per-slot, one wavefront per (tile, slot); grouped,
-// one workgroup per (group of 4 tiles, expert)
-long long gate_up_blocks(int variant, int tiles, long long units) {
-  if (variant == MOE_GATE_UP_EXPERT_GROUPED) return (long long)((tiles + kWavesPerBlock - 1) / kWavesPerBlock) * units;
-  return ((long long)tiles * units + kWavesPerBlock - 1) / kWavesPerBlock;
+// The launcher for (variant, rows); 0 selects the table's choice.  nullptr for
+// an unknown variant or a combination beyond the kernel's limits.
+GateUpLaunch gate_up_launcher(int& variant, int nch, int& rows, int B, int H, int I, int E, int k) {
+  if (variant == 0) variant = gate_up_default_variant(B, H, I, E, k);
+  if (variant == MOE_GATE_UP_PER_SLOT) {
+    if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
+    return gate_up_allowed(nch, rows) ? pick_gate_up(nch, rows) : nullptr;
+  }
+  if (variant == MOE_GATE_UP_EXPERT_GROUPED) {
+    if (rows == 0) rows = grouped_default_rows(H);
+    return grouped_allowed(nch, rows, (long long)B * k, E) ? pick_grouped(nch, rows) : nullptr;
+  }
+  return nullptr;
 }
 
 int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg, const uint8_t* wu,
@@ -195,29 +228,12 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
       overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
     return MOE_ERR_ALIAS;
   const int nch = passes(H);
-  if (variant == 0) variant = gate_up_default_variant(B, H, I, E, k);
-  GateUpLaunch fn = nullptr;
-  long long units = 0;
-  if (variant == MOE_GATE_UP_PER_SLOT) {
-    if (rows == 0) rows = gate_up_default_rows(B, H, I, k);
-    if (!gate_up_allowed(nch, rows)) return MOE_ERR_ARG;
-    fn = pick_gate_up(nch, rows);
-    units = (long long)B * k;
-  } else if (variant == MOE_GATE_UP_EXPERT_GROUPED) {
-    if (rows == 0) rows = grouped_default_rows(H);
-    if (!grouped_allowed(nch, rows, (long long)B * k)) return MOE_ERR_ARG;
-    fn = pick_grouped(nch, rows);
-    units = E;
-  } else {
-    return MOE_ERR_ARG;
-  }
+  GateUpLaunch fn = gate_up_launcher(variant, nch, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
-  const int tiles = (I + rows - 1) / rows;
-  const long long blocks = gate_up_blocks(variant, tiles, units);
+  const long long blocks = fn(false, nullptr, x, ids, wg, sg, wu, su, h, B, H, I, E, k);
   if (blocks * kWavesPerBlock >= (1LL << 31)) return MOE_ERR_SHAPE;
-  const dim3 grid((unsigned)blocks);
   (void)hipGetLastError();
-  fn(grid, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles);
+  fn(true, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -334,12 +350,12 @@ int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
   if (!variant || !rows_per_wave || !workgroups) return MOE_ERR_NULL;
-  const int v = gate_up_default_variant(B, H, I, E, k);
-  const int r = v == MOE_GATE_UP_PER_SLOT ? gate_up_default_rows(B, H, I, k) : grouped_default_rows(H);
-  const long long units = v == MOE_GATE_UP_PER_SLOT ? (long long)B * k : (long long)E;
+  int v = 0, r = 0;
+  GateUpLaunch fn = gate_up_launcher(v, passes(H), r, B, H, I, E, k);
+  if (!fn) return MOE_ERR_ARG;
   *variant = v;
   *rows_per_wave = r;
-  *workgroups = (int)gate_up_blocks(v, (I + r - 1) / r, units);
+  *workgroups = (int)fn(false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, E, k);
   return MOE_OK;
 }
 

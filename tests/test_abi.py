@@ -117,18 +117,24 @@ def test_bad_tuning_arguments():
     assert gu(rows=1, variant=-1) == mg.MOE_ERR_ARG
     assert gu(rows=8, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG      # 2 passes x 8 rows > 8
     assert gu(B=129, rows=1, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG   # B*k > 1024
+    assert gu(E=1025, rows=1, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG  # E > 1024
     assert dn(rows=5) == mg.MOE_ERR_ARG
     assert dn(I=1536, rows=8) == mg.MOE_ERR_ARG      # 12 passes x 8 rows exceeds the register budget
 
 
 def test_plans():
-    for B in (1, 8, 32, 64):
+    for B in (1, 8, 16, 32, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
-        units = B * 8 if v == mg.MOE_GATE_UP_PER_SLOT else 128
-        assert v in (mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED)
-        assert r in (1, 2, 4, 8) and g == -(-((768 + r - 1) // r) * units // 4)
+        assert r in (1, 2, 4, 8)
+        if v == mg.MOE_GATE_UP_PER_SLOT:   # one wavefront per (tile, slot)
+            assert g == -(-((768 + r - 1) // r) * B * 8 // 4)
+        else:                              # persistent: <= 2048 workgroups, <= the possible work items
+            assert v == mg.MOE_GATE_UP_EXPERT_GROUPED
+            assert g == min(2048, min(128, B * 8) * -(-768 // (4 * r)))
+        # grouped once the batch averages two or more slots per expert
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
-    assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
     r, g = mg.moe_decode_down_plan(32, 2048, 768, 128, 8)
     assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * 32 // 4)
     with pytest.raises(mg.MoeDecodeError):
