@@ -110,14 +110,30 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
 
+/* Kernel variants of the down call.
+ *   MOE_DOWN_PER_TOKEN: one wavefront per (R output dimensions, token) --
+ *     the blog post's organisation ("How the two kernels work").  Best while
+ *     few tokens share an expert.
+ *   MOE_DOWN_EXPERT_GROUPED: one workgroup per 8 output dimensions for every
+ *     token; its wavefronts split the routed experts (sorted on the device,
+ *     in LDS), read each routed expert's 8 rows once, and keep every token's
+ *     8 FP32 sums in registers until the workgroup adds them and writes y
+ *     once.  No per-expert output buffer, no combine.  Same outputs; requires
+ *     B <= 64, B*k <= 1024, E <= 1024 and I <= 2048.
+ * The plain call takes the grouped variant once B*k >= 2E and the limits
+ * allow it, else the per-token one. */
+#define MOE_DOWN_PER_TOKEN 1
+#define MOE_DOWN_EXPERT_GROUPED 2
+
 /* Tuning variants of the two calls: the same contract and results within the
  * same tolerance, with the launch shape given explicitly instead of taken
  * from the built-in table.  variant: 0 = the table's choice, else one of the
- * MOE_GATE_UP_* values.  rows_per_wave in {1, 2, 4, 8} is the number of
- * neurons (gate/up) or output dimensions (down) one 64-lane wavefront owns;
- * 0 selects the table's choice.  Combinations beyond the register budget
- * (rows x passes of 1024 elements: <= 16 per-slot, <= 8 grouped; down:
- * passes x (5 rows + 8) <= 224), the grouped variant beyond its limits and
+ * MOE_GATE_UP_* (gate/up) or MOE_DOWN_* (down) values.  rows_per_wave in
+ * {1, 2, 4, 8} is the number of neurons (gate/up) or output dimensions (down)
+ * one 64-lane wavefront owns (the grouped down kernel: 8 only); 0 selects
+ * the table's choice.  Combinations beyond the register budget (rows x
+ * passes of 1024 elements: <= 16 per-slot, <= 8 grouped; per-token down:
+ * passes x (5 rows + 8) <= 224), a grouped variant beyond its limits and
  * unknown variants return MOE_ERR_ARG. */
 int moe_decode_gate_up_ex(const void *x, const int32_t *topk_ids,
                           const uint8_t *w_gate, const uint8_t *s_gate,
@@ -129,13 +145,13 @@ int moe_decode_down_ex(const void *h, const int32_t *topk_ids, const float *topk
                        const uint8_t *w_down, const uint8_t *s_down,
                        void *y_out,
                        int B, int H, int I, int E, int k,
-                       int rows_per_wave, void *stream);
+                       int variant, int rows_per_wave, void *stream);
 
 /* The launch the built-in table picks for a call (for reports): writes the
- * variant (gate/up only), rows_per_wave and the number of workgroups;
- * returns 0 or a negative code. */
+ * variant, rows_per_wave and the number of workgroups; returns 0 or a
+ * negative code. */
 int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int *variant, int *rows_per_wave, int *workgroups);
-int moe_decode_down_plan(int B, int H, int I, int E, int k, int *rows_per_wave, int *workgroups);
+int moe_decode_down_plan(int B, int H, int I, int E, int k, int *variant, int *rows_per_wave, int *workgroups);
 
 /* Bandwidth probes that set the denominator of the efficiency figure (blog
  * post, "Hardware efficiency": peak measured with a copy kernel over

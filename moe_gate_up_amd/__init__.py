@@ -27,6 +27,8 @@ MOE_ERR_ALIAS = -5
 MOE_ERR_ARG = -6
 MOE_GATE_UP_PER_SLOT = 1
 MOE_GATE_UP_EXPERT_GROUPED = 2
+MOE_DOWN_PER_TOKEN = 1
+MOE_DOWN_EXPERT_GROUPED = 2
 
 EXPORTS = (
     "moe_decode_gate_up", "moe_decode_down", "moe_decode_gate_up_ex", "moe_decode_down_ex",
@@ -57,9 +59,9 @@ def lib() -> ctypes.CDLL:
             L.moe_decode_gate_up.argtypes = [P] * 7 + [I] * 5 + [P]
             L.moe_decode_down.argtypes = [P] * 6 + [I] * 5 + [P]
             L.moe_decode_gate_up_ex.argtypes = [P] * 7 + [I] * 7 + [P]
-            L.moe_decode_down_ex.argtypes = [P] * 6 + [I] * 6 + [P]
+            L.moe_decode_down_ex.argtypes = [P] * 6 + [I] * 7 + [P]
             L.moe_decode_gate_up_plan.argtypes = [I] * 5 + [IP, IP, IP]
-            L.moe_decode_down_plan.argtypes = [I] * 5 + [IP, IP]
+            L.moe_decode_down_plan.argtypes = [I] * 5 + [IP, IP, IP]
             L.moe_decode_copy_peak.argtypes = [P, P, S, P]
             L.moe_decode_read_peak.argtypes = [P, S, P, P]
             L.moe_decode_strerror.argtypes = [I]
@@ -128,7 +130,7 @@ def moe_decode_gate_up(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B=None, H
 
 
 def moe_decode_down(h, topk_ids, topk_weights, w_down, s_down, y_out, B=None, H=None, I=None, E=None, k=None,
-                    stream=None, rows_per_wave=None):
+                    stream=None, rows_per_wave=None, variant=None):
     """y_out[b,o] = bf16(sum_j w[b,j] * down row . h[b,j,:]) (see include/moe_decode.h)."""
     T = _types()
     B = h.shape[0] if B is None else B
@@ -142,10 +144,10 @@ def moe_decode_down(h, topk_ids, topk_weights, w_down, s_down, y_out, B=None, H=
         _dev(w_down, "w_down", E * H * I, T["u8"]), _dev(s_down, "s_down", E * H * (I // 32), T["u8"]),
         _dev(y_out, "y_out", B * H, T["bf16"]), B, H, I, E, k,
     ]
-    if rows_per_wave is None:
+    if rows_per_wave is None and variant is None:
         rc = lib().moe_decode_down(*args, _stream(stream))
     else:
-        rc = lib().moe_decode_down_ex(*args, int(rows_per_wave), _stream(stream))
+        rc = lib().moe_decode_down_ex(*args, int(variant or 0), int(rows_per_wave or 0), _stream(stream))
     if rc:
         raise MoeDecodeError(rc, "moe_decode_down")
     return y_out
@@ -161,11 +163,12 @@ def moe_decode_gate_up_plan(B, H, I, E, k):
 
 
 def moe_decode_down_plan(B, H, I, E, k):
-    r, g = ctypes.c_int(), ctypes.c_int()
-    rc = lib().moe_decode_down_plan(B, H, I, E, k, ctypes.byref(r), ctypes.byref(g))
+    """(variant, rows_per_wave, workgroups) the built-in table picks."""
+    v, r, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().moe_decode_down_plan(B, H, I, E, k, ctypes.byref(v), ctypes.byref(r), ctypes.byref(g))
     if rc:
         raise MoeDecodeError(rc, "moe_decode_down_plan")
-    return r.value, g.value
+    return v.value, r.value, g.value
 
 
 def moe_decode_copy_peak(src, dst, stream=None):

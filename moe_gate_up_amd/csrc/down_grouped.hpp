@@ -1,0 +1,199 @@
+// Down kernel, expert-grouped variant (blog post "warp decode", section "How
+// the two kernels work", third and fourth paragraphs, for the arithmetic;
+// section "Warp decode and Composer training" for the regime where several
+// tokens share an expert).  Every output y[b,o] is still one FP32 sum over the
+// token's k routed slots, each slot's dot product scaled by its router weight,
+// written once as bf16, with no per-expert output buffer and no separate
+// combine.  What changes is who reads the rows: a workgroup owns 8
+// consecutive output dimensions o0..o0+7 for every token of the batch, so
+// each routed expert's 8 down rows are read once per layer however many
+// tokens share it (the per-token kernel reads them once per token; at 32
+// tokens x 8 of 128 experts, 2.3 times on average).
+//
+// Steps of one workgroup (NW wavefronts):
+//  1. sort the B*k slots by expert in LDS (slot_sort.hpp);
+//  2. wavefront w takes the routed experts w, w + NW, ...  For each it loads
+//     the expert's 8 rows o0..o0+7 -- contiguous in memory, read as 8 row
+//     passes where lane l takes the 16 bytes at 16 l (+1024 per pass) -- and
+//     their 8 x I/32 E8M0 scales with one dword load per lane (moved to the
+//     lanes that use them with ds_bpermute), then for every slot routed to
+//     the expert loads that slot's h row, forms the 8 dot products (E4M3 ->
+//     bf16, v_dot2c_f32_bf16, v_ldexp_f32 per 16-element partial), sums them
+//     across the wave with one reduce-scatter and adds router weight x sum to
+//     8 FP32 accumulators of the slot's token, which live in lane b of the
+//     wavefront (B <= 64);
+//  3. the NW wavefronts' accumulators meet in LDS and thread (b, r) adds them
+//     in wavefront order and writes y[b, o0 + r].
+// Within a wavefront each token's sum runs over experts in ascending order
+// and, within an expert, slots in slot order; across wavefronts in wavefront
+// order: the result does not depend on timing.  Outputs of a token with an
+// invalid id, or touching a row with a NaN scale code, are NaN.
+#pragma once
+
+#include "slot_sort.hpp"
+
+namespace moe {
+
+constexpr int kDownGroupedRows = 8;        // output dimensions per workgroup
+constexpr int kDownGroupedMaxTokens = 64;  // one token per lane
+constexpr int kDownGroupedSlotsPerRound = 2;
+
+__host__ __device__ constexpr int down_grouped_waves(int np) { return np <= 1 ? 16 : (np == 2 ? 8 : 4); }
+// LDS layout: slot sort | per-wavefront accumulators [NW][8][64] floats | NaN masks [NW][64]
+__host__ __device__ constexpr int down_grouped_lds_bytes(int np, int E, int S) {
+  return slot_sort_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (kDownGroupedRows + 1) * 4;
+}
+
+template <int NP>
+__global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_grouped_w64(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
+    const uint8_t* __restrict__ wd, const uint8_t* __restrict__ sd,
+    uint16_t* __restrict__ y, int B, int H, int I, int E, int k) {
+  constexpr int NW = down_grouped_waves(NP);
+  constexpr int NT = 64 * NW;
+  constexpr int RO = kDownGroupedRows;
+  constexpr int MS = kDownGroupedSlotsPerRound;
+  const int slots = B * k;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int o0 = blockIdx.x * RO;
+  const SlotSort so = sort_slots_by_expert<NT>(lds, ids, slots, E, k);
+  float* accs = reinterpret_cast<float*>(lds + slot_sort_lds_bytes(E, slots));   // [NW][RO][64]
+  uint32_t* nans = reinterpret_cast<uint32_t*>(accs + NW * RO * 64);             // [NW][64]
+
+  const int nblk = I >> 5;
+  uint32_t off[NP];
+  int bias[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    const int o = 1024 * c + 16 * lane;
+    off[c] = (uint32_t)min(o, I - 16);
+    bias[c] = o < I ? kLiveChunk : kDeadChunk;
+  }
+  const uint32_t wbytes = (uint32_t)E * (uint32_t)H * (uint32_t)I;   // < 2^32, checked on the host
+  const rsrc_t wr = make_rsrc(wd, wbytes), sr = make_rsrc(sd, wbytes / 32);
+  const rsrc_t hr = make_rsrc(h, (uint64_t)slots * I * 2), twr = make_rsrc(tw, (uint64_t)slots * 4);
+
+  float acc[RO];   // lane b: token b's partial sums of y[b, o0 + r]
+#pragma unroll
+  for (int r = 0; r < RO; ++r) acc[r] = 0.0f;
+  uint32_t nanacc = 0;   // lane b: bit r set once a NaN scale touched y[b, o0 + r]
+
+  for (int u = w; u < so.n_used; u += NW) {
+    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
+    const int beg = so.begin(e);
+    const int count = so.end(e) - beg;   // >= 1
+    const uint32_t row0 = (uint32_t)e * (uint32_t)H + (uint32_t)o0;
+
+    // the expert's 8 rows and their scales (row0 * nblk is a multiple of 4:
+    // H and o0 are multiples of 8); dword t of lane l holds scale bytes 256 t + 4 l ..
+    u32x4 wv[RO][NP];
+#pragma unroll
+    for (int r = 0; r < RO; ++r)
+#pragma unroll
+      for (int c = 0; c < NP; ++c) wv[r][c] = bload16(wr, off[c], (row0 + r) * (uint32_t)I);
+    uint32_t sw[NP];
+#pragma unroll
+    for (int t = 0; t < NP; ++t)   // past the end of s_down: range-checked, reads zero
+      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
+
+    // h rows and router weights of the first round of slots
+    auto load_round = [&](int m0, u32x4 (&hv)[MS][NP][2], float (&ws)[MS]) {
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const uint32_t ent = so.sorted[beg + min(m0 + m, count - 1)];   // past the end: repeat, unused
+        const uint32_t sl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ent & 0xFFFFu));
+#pragma unroll
+        for (int c = 0; c < NP; ++c) {
+          hv[m][c][0] = bload16(hr, off[c] * 2u, sl * (uint32_t)I * 2u);
+          hv[m][c][1] = bload16(hr, off[c] * 2u + 16u, sl * (uint32_t)I * 2u);
+        }
+        ws[m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(twr, 0u, sl * 4u, 0));
+      }
+    };
+    u32x4 hv[MS][NP][2];
+    float ws[MS];
+    load_round(0, hv, ws);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // scale byte of (row r, pass c) for this lane, and the rows holding a NaN code
+    uint32_t sc[RO][NP];
+    uint32_t nan_rows = 0;
+#pragma unroll
+    for (int r = 0; r < RO; ++r) {
+      uint64_t nl = 0;
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        const uint32_t q = (uint32_t)(r * nblk) + (off[c] >> 5);
+        const int src = (int)(((q >> 2) & 63u) << 2);
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < NP; ++t) {
+          const uint32_t vt = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sw[t]);
+          v = ((q >> 8) == (uint32_t)t) ? vt : v;
+        }
+        sc[r][c] = (v >> ((q & 3u) * 8u)) & 0xFFu;
+        nl |= nan_scale_lanes(sc[r][c]);
+      }
+      nan_rows |= (uint32_t)(nl != 0) << r;
+    }
+
+    for (int m0 = 0; m0 < count; m0 += MS) {
+      if (m0 > 0) load_round(m0, hv, ws);
+      const int nm = min(MS, count - m0);
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        if (m < nm) {
+          // the rows stay E4M3 in registers and are converted per slot: keeping
+          // 8 converted rows would double their registers past the 128 that a
+          // 16-wavefront workgroup allows
+#pragma unroll
+          for (int r = 0; r < RO; ++r)
+#pragma unroll
+            for (int c = 0; c < NP; ++c) asm volatile("" : "+v"(wv[r][c].v[0]), "+v"(wv[r][c].v[1]), "+v"(wv[r][c].v[2]), "+v"(wv[r][c].v[3]));
+          float p[RO];
+#pragma unroll
+          for (int r = 0; r < RO; ++r) {
+            p[r] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NP; ++c) p[r] += apply_e8m0(chunk_dot(wv[r][c], hv[m][c], 0.0f), sc[r][c], bias[c]);
+          }
+          const float tot = wave_reduce_scatter<RO>(p, lane);
+          const int b = __builtin_amdgcn_readfirstlane((int)(so.sorted[beg + m0 + m] >> 16));
+          const float wsm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ws[m])));
+          const float fw = lane == b ? wsm : 0.0f;   // only token b's lane accumulates
+#pragma unroll
+          for (int r = 0; r < RO; ++r) {
+            const float sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tot), scatter_lane<RO>(r)));
+            acc[r] = fmaf(fw, sum, acc[r]);
+          }
+          nanacc |= lane == b ? nan_rows : 0u;
+        }
+      }
+    }
+  }
+
+  // ---- the wavefronts' partial sums meet in LDS; thread (b, r) adds them in wavefront order
+#pragma unroll
+  for (int r = 0; r < RO; ++r) accs[(w * RO + r) * 64 + lane] = acc[r];
+  nans[w * 64 + lane] = nanacc;
+  __syncthreads();
+  for (int t = tid; t < B * RO; t += NT) {
+    const int b = t / RO, r = t - b * RO;
+    float sum = 0.0f;
+    uint32_t nn = 0;
+    for (int v = 0; v < NW; ++v) {
+      sum += accs[(v * RO + r) * 64 + b];
+      nn |= nans[v * 64 + b];
+    }
+    bool nan_out = (nn >> r) & 1u;
+    if (so.n_bad > 0) {   // a token with an invalid id is NaN everywhere
+      for (int j = 0; j < k; ++j) nan_out |= (unsigned)ids[b * k + j] >= (unsigned)E;
+    }
+    y[(size_t)b * H + o0 + r] = f32_to_bf16_rne(nan_out ? qnan() : sum);
+  }
+}
+
+}  // namespace moe

@@ -31,25 +31,22 @@
 // exactly once.
 #pragma once
 
-#include "prims.hpp"
+#include "slot_sort.hpp"
 
 namespace moe {
 
-constexpr int kGroupedMaxSlots = 1024;     // B*k limit of the expert-grouped variant
-constexpr int kGroupedMaxExperts = 1024;   // E limit (per-expert LDS counters)
-constexpr int kGroupedXBytes = 16384;      // LDS for staged activations
+constexpr int kGroupedMaxSlots = kSortMaxSlots;       // B*k limit of the expert-grouped variant
+constexpr int kGroupedMaxExperts = kSortMaxExperts;   // E limit
+constexpr int kGroupedXBytes = 16384;                 // LDS for staged activations
 
-__host__ __device__ constexpr int grouped_a16(int n) { return (n + 15) & ~15; }
 // bytes of one staged x row (1 KB-padded) and rows per chunk
 __host__ __device__ constexpr int grouped_xrow(int H) { return ((2 * H + 1023) / 1024) * 1024; }
 __host__ __device__ constexpr int grouped_chunk(int H) {
   return kGroupedXBytes / grouped_xrow(H) < 1 ? 1 : kGroupedXBytes / grouped_xrow(H);
 }
-// LDS layout: per-expert counters [E] | routed experts [min(E, S)] | sorted
-// slots [S] | 2 counters | staged x [M rows]
+// LDS layout: slot sort | staged x [M rows]
 __host__ __device__ constexpr int grouped_lds_bytes(int E, int S, int H) {
-  return grouped_a16(4 * E) + grouped_a16(4 * (E < S ? E : S)) + grouped_a16(4 * S) + 16 +
-         grouped_chunk(H) * grouped_xrow(H);
+  return slot_sort_lds_bytes(E, S) + grouped_chunk(H) * grouped_xrow(H);
 }
 
 template <int NCH, int R>
@@ -60,66 +57,12 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
     uint16_t* __restrict__ h, int B, int H, int I, int E, int k) {
   const int slots = B * k;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int* cur = reinterpret_cast<int*>(lds);   // per expert: count, then start, then end of its range
-  int* used = reinterpret_cast<int*>(lds + grouped_a16(4 * E));
-  uint32_t* sorted = reinterpret_cast<uint32_t*>(lds + grouped_a16(4 * E) + grouped_a16(4 * min(E, slots)));
-  int* misc = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sorted) + grouped_a16(4 * slots));
-  uint8_t* xs = reinterpret_cast<uint8_t*>(misc) + 16;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-
-  // ---- counting sort of the slots by expert (thread t owns slots t + 256 j)
-  for (int i = tid; i < E; i += 256) cur[i] = 0;
-  if (tid < 4) misc[tid] = 0;
-  __syncthreads();
+  const SlotSort so = sort_slots_by_expert<256>(lds, ids, slots, E, k);
+  uint8_t* xs = lds + slot_sort_lds_bytes(E, slots);   // M rows of x, 2H bytes each, 1 KB-padded
   const rsrc_t idr = make_rsrc(ids, (uint64_t)slots * 4);
-  int sid[4];   // expert, -1 for an invalid id, -2 past the last slot
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int sl = tid + 256 * j;
-    const int v = (int)__builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)min(sl, slots - 1) * 4u, 0, 0));
-    sid[j] = sl < slots ? ((unsigned)v < (unsigned)E ? v : -1) : -2;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (sid[j] >= 0) atomicAdd(&cur[sid[j]], 1);
-    else if (sid[j] == -1) atomicAdd(&misc[1], 1);
-  }
-  __syncthreads();
-  if (w == 0) {   // counts -> starts (exclusive scan), and the routed experts in ascending order
-    int carry = 0, nu = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      const int c = e < E ? cur[e] : 0;
-      int incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d);
-        incl += lane >= d ? t : 0;
-      }
-      if (e < E) cur[e] = carry + incl - c;
-      const uint64_t m = __builtin_amdgcn_ballot_w64(c > 0);
-      if (c > 0) used[nu + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = e;
-      nu += __builtin_popcountll(m);
-      carry += __shfl(incl, 63);
-    }
-    if (lane == 0) misc[0] = nu;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (sid[j] >= 0) {
-      const int sl = tid + 256 * j;
-      sorted[atomicAdd(&cur[sid[j]], 1)] = (uint32_t)sl | ((uint32_t)(sl / k) << 16);
-    }
-  }
-  __syncthreads();
-  // cur[e] is now the end of e's range; its start is cur[e - 1] (0 for e = 0)
-  const int n_used = __builtin_amdgcn_readfirstlane(misc[0]);
-  const int n_bad = __builtin_amdgcn_readfirstlane(misc[1]);
 
   // ---- per-lane constants of the R-row passes
   uint32_t off[NCH];
@@ -144,13 +87,13 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
 
   // ---- work items: (routed expert u, group of 4 tiles g)
   const int n_grp = (I + 4 * R - 1) / (4 * R);
-  const int n_items = n_used * n_grp;
+  const int n_items = so.n_used * n_grp;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int u = __builtin_amdgcn_readfirstlane(item / n_grp);   // VALU division, uniform result
     const int g = item - u * n_grp;
-    const int e = __builtin_amdgcn_readfirstlane(used[u]);
-    const int beg = e > 0 ? __builtin_amdgcn_readfirstlane(cur[e - 1]) : 0;
-    const int count = __builtin_amdgcn_readfirstlane(cur[e]) - beg;   // >= 1
+    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
+    const int beg = so.begin(e);
+    const int count = so.end(e) - beg;   // >= 1
     const int n0 = (g * 4 + w) * R;   // this wavefront's first neuron (may be >= I: nothing stored)
 
     u32x4 gw[R][NCH], uw[R][NCH];
@@ -178,7 +121,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
       const int nm = min(M, count - m0);
       for (int m = 0; m < nm; ++m) {
         const uint32_t xo =
-            (uint32_t)__builtin_amdgcn_readfirstlane((int)(sorted[beg + m0 + m] >> 16)) * (uint32_t)H * 2u;
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(so.sorted[beg + m0 + m] >> 16)) * (uint32_t)H * 2u;
         for (int p = w; p < pieces; p += 4)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xs + m * XS + 1024 * p),
                                                    16, xo + 1024u * p + 16u * lane, 0, 0, 0);
@@ -206,7 +149,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
         nan_out = r_out >= 0 && ((nan_rows >> r_out) & 1);
       }
       for (int m = 0; m < nm; ++m) {
-        const int s = (int)(sorted[beg + m0 + m] & 0xFFFFu);
+        const int s = (int)(so.sorted[beg + m0 + m] & 0xFFFFu);
         u32x4 xa[NCH][2];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -235,7 +178,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   }
 
   // ---- slots with an invalid expert id: NaN in every neuron
-  if (n_bad > 0) {
+  if (so.n_bad > 0) {
     for (int sl = blockIdx.x; sl < slots; sl += gridDim.x) {
       const int v = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)sl * 4u, 0, 0));
       if ((unsigned)__builtin_amdgcn_readfirstlane(v) >= (unsigned)E)

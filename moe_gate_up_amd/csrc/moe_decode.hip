@@ -7,6 +7,7 @@
 
 #include "moe_decode.h"
 #include "down.hpp"
+#include "down_grouped.hpp"
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
 #include "peak.hpp"
@@ -253,16 +254,25 @@ int down_default_rows(int B, int H, int I, int k) {
   return r;
 }
 
+// Down launchers, like the gate/up ones, return their number of workgroups
+// and launch only when `go` is set.
+//
+// Per-token grid: one wavefront per (tile of R outputs, token), 4 tiles of one
+// token per workgroup; dynamic LDS: h[b] of the workgroup's token, 2*k*I <= 32 KB.
 template <int NP, int R>
-void launch_down_t(dim3 grid, hipStream_t st, const void* h, const int32_t* ids, const float* tw, const uint8_t* wd,
-                   const uint8_t* sd, void* y, int B, int H, int I, int E, int k, int tiles) {
-  // dynamic LDS: h[b] of the workgroup's token, 2*k*I <= 32 KB
-  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), grid, dim3(64 * kWavesPerBlock), (unsigned)(2 * k * I), st,
-                     static_cast<const uint16_t*>(h), ids, tw, wd, sd, static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
+long long launch_down_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
+                        const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
+  const int tiles = (H + R - 1) / R;
+  const long long blocks = ((long long)tiles * B + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (!go) return blocks;
+  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+                     (unsigned)(2 * k * I), st, static_cast<const uint16_t*>(h), ids, tw, wd, sd,
+                     static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
+  return blocks;
 }
 
-using DownLaunch = void (*)(dim3, hipStream_t, const void*, const int32_t*, const float*, const uint8_t*,
-                            const uint8_t*, void*, int, int, int, int, int, int);
+using DownLaunch = long long (*)(bool, hipStream_t, const void*, const int32_t*, const float*, const uint8_t*,
+                                 const uint8_t*, void*, int, int, int, int, int);
 
 template <int NP, int R>
 DownLaunch down_fn() {
@@ -292,8 +302,65 @@ DownLaunch pick_down(int np, int r) {
   return pick_down_np(np, r, std::make_integer_sequence<int, kMaxDownPasses>{});
 }
 
+// ---------------------------------------------------------------- down, expert-grouped
+// One workgroup per 8 output dimensions, passes of 1024 elements over I
+// (<= 2: the 8 rows take 64 VGPRs per pass once converted, and the workgroup
+// shrinks from 16 to 8 wavefronts for two passes); one token per lane: B <= 64.
+constexpr int kMaxDownGroupedPasses = 2;
+bool down_grouped_allowed(int I, long long slots, int B, int E) {
+  return passes(I) <= kMaxDownGroupedPasses && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts &&
+         B <= moe::kDownGroupedMaxTokens;
+}
+
+template <int NP>
+long long launch_down_grouped_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
+                                const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
+  const long long blocks = H / moe::kDownGroupedRows;   // H is a multiple of 32
+  if (!go) return blocks;
+  hipLaunchKernelGGL((moe::moe_down_expert_grouped_w64<NP>), dim3((unsigned)blocks),
+                     dim3(64 * moe::down_grouped_waves(NP)),
+                     (unsigned)moe::down_grouped_lds_bytes(NP, E, B * k), st, static_cast<const uint16_t*>(h), ids,
+                     tw, wd, sd, static_cast<uint16_t*>(y), B, H, I, E, k);
+  return blocks;
+}
+
+DownLaunch pick_down_grouped(int np) {
+  switch (np) {
+    case 1: return launch_down_grouped_t<1>;
+    case 2: return launch_down_grouped_t<2>;
+  }
+  return nullptr;
+}
+
+// Variant table (graph-timed sweeps on MI355X, H = 2048 and 4096, 128
+// experts, top-8, uniform routing): the per-token kernel while few tokens
+// share an expert, the expert-grouped one from two slots per expert on.
+int down_default_variant(int B, int H, int I, int E, int k) {
+  (void)H;
+  const long long slots = (long long)B * k;
+  if (slots >= 2LL * E && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
+  return MOE_DOWN_PER_TOKEN;
+}
+
+// The launcher for (variant, rows); 0 selects the table's choice.  The
+// grouped kernel always takes 8 rows per wavefront.
+DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, int k) {
+  if (variant == 0) variant = down_default_variant(B, H, I, E, k);
+  if (variant == MOE_DOWN_PER_TOKEN) {
+    const int np = passes((long long)k * I);
+    if (rows == 0) rows = down_default_rows(B, H, I, k);
+    return down_allowed(np, rows) ? pick_down(np, rows) : nullptr;
+  }
+  if (variant == MOE_DOWN_EXPERT_GROUPED) {
+    if (rows == 0) rows = moe::kDownGroupedRows;
+    if (rows != moe::kDownGroupedRows || !down_grouped_allowed(I, (long long)B * k, B, E)) return nullptr;
+    return pick_down_grouped(passes(I));
+  }
+  return nullptr;
+}
+
 int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t* wd, const uint8_t* sd, void* y,
-              int B, int H, int I, int E, int k, int rows, void* stream) {
+              int B, int H, int I, int E, int k, int variant, int rows, void* stream) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
   if (B == 0) return MOE_OK;
@@ -304,16 +371,10 @@ int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t*
   if (overlaps(y, yb, h, (size_t)B * k * I * 2) || overlaps(y, yb, ids, (size_t)B * k * 4) ||
       overlaps(y, yb, tw, (size_t)B * k * 4) || overlaps(y, yb, wd, wb) || overlaps(y, yb, sd, wb / 32))
     return MOE_ERR_ALIAS;
-  const int np = passes((long long)k * I);
-  if (rows == 0) rows = down_default_rows(B, H, I, k);
-  if (!down_allowed(np, rows)) return MOE_ERR_ARG;
-  DownLaunch fn = pick_down(np, rows);
+  DownLaunch fn = down_launcher(variant, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
-  const int tiles = (H + rows - 1) / rows;
-  const long long waves = (long long)tiles * B;
-  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
   (void)hipGetLastError();
-  fn(grid, static_cast<hipStream_t>(stream), h, ids, tw, wd, sd, y, B, H, I, E, k, tiles);
+  fn(true, static_cast<hipStream_t>(stream), h, ids, tw, wd, sd, y, B, H, I, E, k);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -336,14 +397,14 @@ int moe_decode_gate_up_ex(const void* x, const int32_t* topk_ids, const uint8_t*
 
 int moe_decode_down(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
                     const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, void* stream) {
-  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, 0, stream);
+  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, 0, 0, stream);
 }
 
 int moe_decode_down_ex(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
-                       const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, int rows_per_wave,
-                       void* stream) {
-  if (rows_per_wave < 0) return MOE_ERR_ARG;
-  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, rows_per_wave, stream);
+                       const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, int variant,
+                       int rows_per_wave, void* stream) {
+  if (rows_per_wave < 0 || variant < 0) return MOE_ERR_ARG;
+  return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, variant, rows_per_wave, stream);
 }
 
 int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int* rows_per_wave, int* workgroups) {
@@ -359,13 +420,16 @@ int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int
   return MOE_OK;
 }
 
-int moe_decode_down_plan(int B, int H, int I, int E, int k, int* rows_per_wave, int* workgroups) {
+int moe_decode_down_plan(int B, int H, int I, int E, int k, int* variant, int* rows_per_wave, int* workgroups) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
-  if (!rows_per_wave || !workgroups) return MOE_ERR_NULL;
-  const int r = down_default_rows(B, H, I, k);
+  if (!variant || !rows_per_wave || !workgroups) return MOE_ERR_NULL;
+  int v = 0, r = 0;
+  DownLaunch fn = down_launcher(v, r, B, H, I, E, k);
+  if (!fn) return MOE_ERR_ARG;
+  *variant = v;
   *rows_per_wave = r;
-  *workgroups = (int)((((long long)(H + r - 1) / r) * B + kWavesPerBlock - 1) / kWavesPerBlock);
+  *workgroups = (int)fn(false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, E, k);
   return MOE_OK;
 }
 

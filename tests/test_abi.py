@@ -57,12 +57,12 @@ def gu(x=A, ids=A + 1 * S, wg=A + 2 * S, sg=A + 3 * S, wu=A + 4 * S, su=A + 5 * 
 
 
 def dn(h=A, ids=A + 1 * S, tw=A + 2 * S, wd=A + 3 * S, sd=A + 4 * S, y=A + 5 * S,
-       B=2, H=2048, I=768, E=128, k=8, rows=None):
+       B=2, H=2048, I=768, E=128, k=8, rows=None, variant=0):
     L = mg.lib()
     args = [ctypes.c_void_p(p) for p in (h, ids, tw, wd, sd, y)] + [B, H, I, E, k]
     if rows is None:
         return L.moe_decode_down(*args, None)
-    return L.moe_decode_down_ex(*args, rows, None)
+    return L.moe_decode_down_ex(*args, variant, rows, None)
 
 
 @pytest.mark.parametrize("fn", [gu, dn])
@@ -120,6 +120,13 @@ def test_bad_tuning_arguments():
     assert gu(E=1025, rows=1, variant=mg.MOE_GATE_UP_EXPERT_GROUPED) == mg.MOE_ERR_ARG  # E > 1024
     assert dn(rows=5) == mg.MOE_ERR_ARG
     assert dn(I=1536, rows=8) == mg.MOE_ERR_ARG      # 12 passes x 8 rows exceeds the register budget
+    assert dn(rows=1, variant=3) == mg.MOE_ERR_ARG
+    assert dn(rows=1, variant=-1) == mg.MOE_ERR_ARG
+    G = mg.MOE_DOWN_EXPERT_GROUPED
+    assert dn(rows=4, variant=G) == mg.MOE_ERR_ARG                # the grouped kernel takes 8 rows
+    assert dn(B=65, k=8, rows=8, variant=G) == mg.MOE_ERR_ARG     # B > 64
+    assert dn(I=2080, k=2, rows=8, variant=G) == mg.MOE_ERR_ARG   # I beyond 2 passes
+    assert dn(E=1025, rows=0, variant=G) == mg.MOE_ERR_ARG        # E > 1024
 
 
 def test_plans():
@@ -135,8 +142,14 @@ def test_plans():
         assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
-    r, g = mg.moe_decode_down_plan(32, 2048, 768, 128, 8)
-    assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * 32 // 4)
+    for B in (1, 8, 16, 32, 64):
+        v, r, g = mg.moe_decode_down_plan(B, 2048, 768, 128, 8)
+        if v == mg.MOE_DOWN_PER_TOKEN:     # one wavefront per (tile, token)
+            assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * B // 4)
+        else:                              # one workgroup per 8 output dimensions
+            assert v == mg.MOE_DOWN_EXPERT_GROUPED and r == 8 and g == 2048 // 8
+        assert (v == mg.MOE_DOWN_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
+    assert mg.moe_decode_down_plan(100, 2048, 768, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN   # B > 64
     with pytest.raises(mg.MoeDecodeError):
         mg.moe_decode_gate_up_plan(1, 100, 768, 128, 8)
 

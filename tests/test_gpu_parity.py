@@ -48,13 +48,21 @@ class DevLayer:
         return (L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
 
 
+# kernel families: (gate/up variant, down variant); None = the built-in table's choice
+PER_SLOT = (mg.MOE_GATE_UP_PER_SLOT, mg.MOE_DOWN_PER_TOKEN)
+GROUPED = (mg.MOE_GATE_UP_EXPERT_GROUPED, mg.MOE_DOWN_EXPERT_GROUPED)
+FAMILIES = [PER_SLOT, GROUPED]
+BOTH = (None, PER_SLOT, GROUPED)
+
+
 def run_gpu(D, x, ids, w, dev, rows_gu=None, rows_dn=None, stream=None, variant=None):
     B, k = ids.shape
+    vg, vd = variant if variant is not None else (None, None)
     xd, idd, wdv = _t(x, dev), _t(ids, dev), _t(w, dev)
     h = torch.empty((B, k, D.I), dtype=torch.int16, device=dev)
     y = torch.empty((B, D.H), dtype=torch.int16, device=dev)
-    mg.moe_decode_gate_up(xd, idd, D.wg, D.sg, D.wu, D.su, h, stream=stream, rows_per_wave=rows_gu, variant=variant)
-    mg.moe_decode_down(h, idd, wdv, D.wd, D.sd, y, stream=stream, rows_per_wave=rows_dn)
+    mg.moe_decode_gate_up(xd, idd, D.wg, D.sg, D.wu, D.su, h, stream=stream, rows_per_wave=rows_gu, variant=vg)
+    mg.moe_decode_down(h, idd, wdv, D.wd, D.sd, y, stream=stream, rows_per_wave=rows_dn, variant=vd)
     torch.cuda.synchronize()
     return h.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16)
 
@@ -72,7 +80,8 @@ def check(h, y, h_ref, y_ref, B, k, what=""):
 
 # --------------------------------------------------------------- decode path
 @pytest.mark.parametrize("scale", [127, 120, 134, 1, 0, 253, 255])
-def test_every_e4m3_code_through_down_kernel(dev, scale):
+@pytest.mark.parametrize("dvariant", [mg.MOE_DOWN_PER_TOKEN, mg.MOE_DOWN_EXPERT_GROUPED])
+def test_every_e4m3_code_through_down_kernel(dev, scale, dvariant):
     """y[o] = w * dec(code o) * 2^(scale-127) * h[0]: one product per output, so exact."""
     E, H, I, k, B = 1, 256, 32, 1, 1
     wd = np.zeros((E, H, I), np.uint8)
@@ -83,7 +92,7 @@ def test_every_e4m3_code_through_down_kernel(dev, scale):
     ids = np.zeros((B, k), np.int32)
     w = np.ones((B, k), np.float32)
     y = torch.empty((B, H), dtype=torch.int16, device=dev)
-    mg.moe_decode_down(_t(h, dev), _t(ids, dev), _t(w, dev), _t(wd, dev), _t(sd, dev), y)
+    mg.moe_decode_down(_t(h, dev), _t(ids, dev), _t(w, dev), _t(wd, dev), _t(sd, dev), y, variant=dvariant)
     torch.cuda.synchronize()
     got = y.cpu().numpy().view(np.uint16)[0]
     ref = oracle.down(h, ids, w, wd, sd)[0]
@@ -116,15 +125,19 @@ def small_layers(dev):
 
 @pytest.mark.parametrize("shape", SMALL, ids=[str(s) for s in SMALL])
 @pytest.mark.parametrize("rows", [None, 1, 2, 4, 8])
-@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+@pytest.mark.parametrize("variant", FAMILIES, ids=["per_slot", "grouped"])
 def test_small_shapes_all_variants(dev, small_layers, shape, rows, variant):
     B, H, I, E, k = shape
     D = small_layers[shape]
-    # register-feasible variants only (passes of 1024 elements per lane group)
+    # register-feasible variants only (passes of 1024 elements per lane group);
+    # the grouped down kernel always takes 8 rows
     n_gu, n_dn = -(-H // 1024), -(-(k * I) // 1024)
-    cap = 16 if variant == mg.MOE_GATE_UP_PER_SLOT else 8
+    cap = 16 if variant == PER_SLOT else 8
     rows_gu = rows if rows is None or rows * n_gu <= cap else None
-    rows_dn = rows if rows is None or n_dn * (5 * rows + 8) <= 224 else None
+    if variant == PER_SLOT:
+        rows_dn = rows if rows is None or n_dn * (5 * rows + 8) <= 224 else None
+    else:
+        rows_dn = rows if rows == 8 else None
     x = mi.make_x(7, B, H)
     ids, w = mi.route_uniform(7, B, E, k)
     h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn, variant=variant)
@@ -132,7 +145,7 @@ def test_small_shapes_all_variants(dev, small_layers, shape, rows, variant):
     check(h, y, h_ref, y_ref, B, k, f"{shape} rows={rows} variant={variant}")
 
 
-@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+@pytest.mark.parametrize("variant", FAMILIES, ids=["per_slot", "grouped"])
 def test_duplicate_ids_within_a_token(dev, small_layers, variant):
     """A token may list one expert twice; each slot is computed and summed on its own."""
     shape = (3, 2048, 96, 16, 8)
@@ -162,9 +175,6 @@ def _full(D, config, B, routing, dev, it=0, variants=(None,)):
     for v in variants:
         h, y = run_gpu(D, x, ids, w, dev, variant=v)
         check(h, y, h_ref, y_ref, B, 8, f"config{config} B={B} {routing} variant={v}")
-
-
-BOTH = (None, mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED)
 
 
 def test_config1_single_layer_b1(dev, s1):
@@ -227,12 +237,19 @@ def test_output_coverage_and_guards(dev, s1):
     assert not np.any(hb[G:-G] == 0xFFFF) and not np.any(yb[G:-G] == 0xFFFF)
 
 
-def test_deterministic(dev, s1):
-    x = mi.make_x(66, 8, s1.H)
-    ids, w = mi.route_uniform(66, 8, s1.E, 8)
-    a = run_gpu(s1, x, ids, w, dev)
-    b = run_gpu(s1, x, ids, w, dev)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+@pytest.mark.parametrize("B", [8, 32])
+def test_deterministic(dev, s1, B):
+    """Same inputs, same bits, for both kernel families (the grouped kernels sort
+    slots with LDS atomics; the sort is put back in slot order).  Token 0 lists
+    one expert three times, so a timing-dependent slot order would show."""
+    x = mi.make_x(66, B, s1.H)
+    ids, w = mi.route_uniform(66, B, s1.E, 8)
+    ids[0, 1] = ids[0, 2] = ids[0, 0]
+    for v in BOTH:
+        a = run_gpu(s1, x, ids, w, dev, variant=v)
+        for _ in range(3):
+            b = run_gpu(s1, x, ids, w, dev, variant=v)
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), v
 
 
 def test_nondefault_stream(dev, s1):
@@ -284,7 +301,7 @@ def test_empty_batch(dev, s1):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("variant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+@pytest.mark.parametrize("variant", FAMILIES, ids=["per_slot", "grouped"])
 def test_out_of_range_ids_give_nan_not_faults(dev, s1, variant):
     B, k = 4, 8
     x = mi.make_x(88, B, s1.H)
