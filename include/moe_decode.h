@@ -114,14 +114,15 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *   MOE_DOWN_PER_TOKEN: one wavefront per (R output dimensions, token) --
  *     the blog post's organisation ("How the two kernels work").  Best while
  *     few tokens share an expert.
- *   MOE_DOWN_EXPERT_GROUPED: one workgroup per 8 output dimensions for every
- *     token; its wavefronts split the routed experts (sorted on the device,
- *     in LDS), read each routed expert's 8 rows once, and keep every token's
- *     8 FP32 sums in registers until the workgroup adds them and writes y
- *     once.  No per-expert output buffer, no combine.  Same outputs; requires
+ *   MOE_DOWN_EXPERT_GROUPED: one workgroup per 8 output dimensions (4 for
+ *     I > 1024) for every token; its wavefronts split the routed experts
+ *     (sorted on the device, in LDS), read each routed expert's rows once,
+ *     and keep every token's FP32 sums in registers until the workgroup adds
+ *     them and writes y once.  No per-expert output buffer, no combine.  Same
+ *     outputs; requires
  *     B <= 64, B*k <= 1024, E <= 1024 and I <= 2048.
- * The plain call takes the grouped variant once B*k >= 2E and the limits
- * allow it, else the per-token one. */
+ * The plain call takes the grouped variant once B*k >= 2E (B*k >= E when
+ * I > 1024) and the limits allow it, else the per-token one. */
 #define MOE_DOWN_PER_TOKEN 1
 #define MOE_DOWN_EXPERT_GROUPED 2
 
@@ -130,7 +131,8 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  * from the built-in table.  variant: 0 = the table's choice, else one of the
  * MOE_GATE_UP_* (gate/up) or MOE_DOWN_* (down) values.  rows_per_wave in
  * {1, 2, 4, 8} is the number of neurons (gate/up) or output dimensions (down)
- * one 64-lane wavefront owns (the grouped down kernel: 8 only); 0 selects
+ * one 64-lane wavefront owns (the grouped down kernel: 8 for I <= 1024,
+ * else 4); 0 selects
  * the table's choice.  Combinations beyond the register budget (rows x
  * passes of 1024 elements: <= 16 per-slot, <= 8 grouped; per-token down:
  * passes x (5 rows + 8) <= 224), a grouped variant beyond its limits and

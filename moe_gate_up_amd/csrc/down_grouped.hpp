@@ -4,26 +4,27 @@
 // tokens share an expert).  Every output y[b,o] is still one FP32 sum over the
 // token's k routed slots, each slot's dot product scaled by its router weight,
 // written once as bf16, with no per-expert output buffer and no separate
-// combine.  What changes is who reads the rows: a workgroup owns 8
-// consecutive output dimensions o0..o0+7 for every token of the batch, so
-// each routed expert's 8 down rows are read once per layer however many
-// tokens share it (the per-token kernel reads them once per token; at 32
+// combine.  What changes is who reads the rows: a workgroup owns RO (8, or
+// 4 for I > 1024) consecutive output dimensions for every token of the
+// batch, so each routed expert's RO down rows are read once per layer however
+// many tokens share it (the per-token kernel reads them once per token; at 32
 // tokens x 8 of 128 experts, 2.3 times on average).
 //
 // Steps of one workgroup (NW wavefronts):
-//  1. sort the B*k slots by expert in LDS (slot_sort.hpp);
+//  1. sort the B*k slots by expert in LDS (slot_sort.hpp); each wavefront's
+//     first expert's rows are requested between the two phases of the sort;
 //  2. wavefront w takes the routed experts w, w + NW, ...  For each it loads
-//     the expert's 8 rows o0..o0+7 -- contiguous in memory, read as 8 row
-//     passes where lane l takes the 16 bytes at 16 l (+1024 per pass) -- and
-//     their 8 x I/32 E8M0 scales with one dword load per lane (moved to the
+//     the expert's RO rows -- contiguous in memory, read as RO row passes
+//     where lane l takes the 16 bytes at 16 l (+1024 per pass) -- and their
+//     RO x I/32 E8M0 scales with one dword load per lane (moved to the
 //     lanes that use them with ds_bpermute), then for every slot routed to
-//     the expert loads that slot's h row, forms the 8 dot products (E4M3 ->
+//     the expert loads that slot's h row, forms the RO dot products (E4M3 ->
 //     bf16, v_dot2c_f32_bf16, v_ldexp_f32 per 16-element partial), sums them
 //     across the wave with one reduce-scatter and adds router weight x sum to
-//     8 FP32 accumulators of the slot's token, which live in lane b of the
+//     RO FP32 accumulators of the slot's token, which live in lane b of the
 //     wavefront (B <= 64);
 //  3. the NW wavefronts' accumulators meet in LDS and thread (b, r) adds them
-//     in wavefront order and writes y[b, o0 + r].
+//     in wavefront order and writes y[b, o0 + r] once.
 // Within a wavefront each token's sum runs over experts in ascending order
 // and, within an expert, slots in slot order; across wavefronts in wavefront
 // order: the result does not depend on timing.  Outputs of a token with an
@@ -34,14 +35,17 @@
 
 namespace moe {
 
-constexpr int kDownGroupedRows = 8;        // output dimensions per workgroup
 constexpr int kDownGroupedMaxTokens = 64;  // one token per lane
 constexpr int kDownGroupedSlotsPerRound = 2;
 
-__host__ __device__ constexpr int down_grouped_waves(int np) { return np <= 1 ? 16 : (np == 2 ? 8 : 4); }
-// LDS layout: slot sort | per-wavefront accumulators [NW][8][64] floats | NaN masks [NW][64]
+// Launch shape by passes of 1024 elements over I (graph-timed on MI355X):
+// one pass (I <= 1024): 8 output dimensions per workgroup of 16 wavefronts;
+// two passes: 4 output dimensions per workgroup of 8 wavefronts.
+__host__ __device__ constexpr int down_grouped_rows(int np) { return np <= 1 ? 8 : 4; }
+__host__ __device__ constexpr int down_grouped_waves(int np) { return np <= 1 ? 16 : 8; }
+// LDS layout: slot sort | per-wavefront accumulators [NW][RO][64] floats | NaN masks [NW][64]
 __host__ __device__ constexpr int down_grouped_lds_bytes(int np, int E, int S) {
-  return slot_sort_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (kDownGroupedRows + 1) * 4;
+  return slot_sort_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (down_grouped_rows(np) + 1) * 4;
 }
 
 template <int NP>
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
     uint16_t* __restrict__ y, int B, int H, int I, int E, int k) {
   constexpr int NW = down_grouped_waves(NP);
   constexpr int NT = 64 * NW;
-  constexpr int RO = kDownGroupedRows;
+  constexpr int RO = down_grouped_rows(NP);
   constexpr int MS = kDownGroupedSlotsPerRound;
   const int slots = B * k;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -59,7 +63,9 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int o0 = blockIdx.x * RO;
-  const SlotSort so = sort_slots_by_expert<NT>(lds, ids, slots, E, k);
+  SlotSorter<NT> sorter;
+  sorter.count(lds, ids, slots, E, k);
+  const SlotSort& so = sorter.o;
   float* accs = reinterpret_cast<float*>(lds + slot_sort_lds_bytes(E, slots));   // [NW][RO][64]
   uint32_t* nans = reinterpret_cast<uint32_t*>(accs + NW * RO * 64);             // [NW][64]
 
@@ -81,23 +87,26 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   for (int r = 0; r < RO; ++r) acc[r] = 0.0f;
   uint32_t nanacc = 0;   // lane b: bit r set once a NaN scale touched y[b, o0 + r]
 
-  for (int u = w; u < so.n_used; u += NW) {
-    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
-    const int beg = so.begin(e);
-    const int count = so.end(e) - beg;   // >= 1
+  // the expert's RO rows and their scales (row0 * nblk is a multiple of 4: H
+  // and o0 are multiples of 4); dword t of lane l holds scale bytes 256 t + 4 l ..
+  u32x4 wv[RO][NP];
+  uint32_t sw[NP];
+  auto load_rows = [&](int e) {   // scales first: they are needed first
     const uint32_t row0 = (uint32_t)e * (uint32_t)H + (uint32_t)o0;
-
-    // the expert's 8 rows and their scales (row0 * nblk is a multiple of 4:
-    // H and o0 are multiples of 8); dword t of lane l holds scale bytes 256 t + 4 l ..
-    u32x4 wv[RO][NP];
+#pragma unroll
+    for (int t = 0; t < NP; ++t)   // past the end of s_down: range-checked, reads zero
+      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
 #pragma unroll
     for (int r = 0; r < RO; ++r)
 #pragma unroll
       for (int c = 0; c < NP; ++c) wv[r][c] = bload16(wr, off[c], (row0 + r) * (uint32_t)I);
-    uint32_t sw[NP];
-#pragma unroll
-    for (int t = 0; t < NP; ++t)   // past the end of s_down: range-checked, reads zero
-      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
+  };
+  // One routed expert with its rows already requested: its slots' h rows,
+  // dot products and accumulation.
+  auto process = [&](int u) {
+    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
+    const int beg = so.begin(e);
+    const int count = so.end(e) - beg;   // >= 1
 
     // h rows and router weights of the first round of slots
     auto load_round = [&](int m0, u32x4 (&hv)[MS][NP][2], float (&ws)[MS]) {
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
       for (int m = 0; m < MS; ++m) {
         if (m < nm) {
           // the rows stay E4M3 in registers and are converted per slot: keeping
-          // 8 converted rows would double their registers past the 128 that a
+          // them converted would double their registers past the 128 that a
           // 16-wavefront workgroup allows
 #pragma unroll
           for (int r = 0; r < RO; ++r)
@@ -172,7 +181,30 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
           nanacc |= lane == b ? nan_rows : 0u;
         }
       }
+      // An unconditional use of every load of the round, after all of its
+      // consumers: it keeps the compiler from sinking a slot's loads into that
+      // slot's branch (which put their latency behind the previous slot's
+      // work); by now the values have arrived, so it costs no wait.
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+#pragma unroll
+        for (int c = 0; c < NP; ++c) asm volatile("" ::"v"(hv[m][c][0].v[0]), "v"(hv[m][c][1].v[0]));
+        asm volatile("" ::"v"(ws[m]));
+      }
     }
+    };
+
+  // The first expert's rows go out before the slots are scattered.  The load
+  // is unconditional (a wavefront without an expert reads one it will not
+  // use) and the first expert is processed outside the loop, so no row
+  // register is merged across a branch or carried around the loop: either
+  // made the compiler wait for the loads before the scatter.
+  load_rows(so.n_used > 0 ? __builtin_amdgcn_readfirstlane(so.used[min(w, so.n_used - 1)]) : 0);
+  sorter.scatter();
+  if (w < so.n_used) process(w);
+  for (int u = w + NW; u < so.n_used; u += NW) {
+    load_rows(__builtin_amdgcn_readfirstlane(so.used[u]));
+    process(u);
   }
 
   // ---- the wavefronts' partial sums meet in LDS; thread (b, r) adds them in wavefront order

@@ -60,7 +60,10 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  const SlotSort so = sort_slots_by_expert<256>(lds, ids, slots, E, k);
+  SlotSorter<256> sorter;
+  sorter.count(lds, ids, slots, E, k);
+  sorter.scatter();
+  const SlotSort& so = sorter.o;
   uint8_t* xs = lds + slot_sort_lds_bytes(E, slots);   // M rows of x, 2H bytes each, 1 KB-padded
   const rsrc_t idr = make_rsrc(ids, (uint64_t)slots * 4);
 
@@ -88,16 +91,9 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   // ---- work items: (routed expert u, group of 4 tiles g)
   const int n_grp = (I + 4 * R - 1) / (4 * R);
   const int n_items = so.n_used * n_grp;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int u = __builtin_amdgcn_readfirstlane(item / n_grp);   // VALU division, uniform result
-    const int g = item - u * n_grp;
-    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
-    const int beg = so.begin(e);
-    const int count = so.end(e) - beg;   // >= 1
-    const int n0 = (g * 4 + w) * R;   // this wavefront's first neuron (may be >= I: nothing stored)
-
-    u32x4 gw[R][NCH], uw[R][NCH];
-    uint32_t gsc[R][NCH], usc[R][NCH];
+  u32x4 gw[R][NCH], uw[R][NCH];
+  uint32_t gsc[R][NCH], usc[R][NCH];
+  auto load_rows = [&](int e, int n0) {   // the wavefront's R gate and R up rows of expert e
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t row = (uint32_t)(e * I + min(n0 + r, I - 1));   // ragged: clamp, not stored
@@ -110,6 +106,18 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
         usc[r][c] = bload8(usr, off[c] >> 5, soff);
       }
     }
+  };
+  auto item_expert = [&](int item, int& e, int& n0) {
+    const int u = __builtin_amdgcn_readfirstlane(item / n_grp);   // VALU division, uniform result
+    e = __builtin_amdgcn_readfirstlane(so.used[u]);
+    n0 = ((item - u * n_grp) * 4 + w) * R;   // this wavefront's first neuron (may be >= I: nothing stored)
+  };
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    int e, n0;
+    item_expert(item, e, n0);
+    load_rows(e, n0);
+    const int beg = so.begin(e);
+    const int count = so.end(e) - beg;   // >= 1
 
     // x rows are copied global -> LDS without passing through registers
     // (buffer loads with the LDS bit: lane l's 16 bytes land at the

@@ -303,9 +303,9 @@ DownLaunch pick_down(int np, int r) {
 }
 
 // ---------------------------------------------------------------- down, expert-grouped
-// One workgroup per 8 output dimensions, passes of 1024 elements over I
-// (<= 2: the 8 rows take 64 VGPRs per pass once converted, and the workgroup
-// shrinks from 16 to 8 wavefronts for two passes); one token per lane: B <= 64.
+// One workgroup per 8 (I <= 1024) or 4 output dimensions, at most two passes
+// of 1024 elements over I (the rows stay in registers for every slot of an
+// expert); one token per lane: B <= 64.
 constexpr int kMaxDownGroupedPasses = 2;
 bool down_grouped_allowed(int I, long long slots, int B, int E) {
   return passes(I) <= kMaxDownGroupedPasses && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts &&
@@ -315,7 +315,7 @@ bool down_grouped_allowed(int I, long long slots, int B, int E) {
 template <int NP>
 long long launch_down_grouped_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
                                 const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
-  const long long blocks = H / moe::kDownGroupedRows;   // H is a multiple of 32
+  const long long blocks = H / moe::down_grouped_rows(NP);   // H is a multiple of 32
   if (!go) return blocks;
   hipLaunchKernelGGL((moe::moe_down_expert_grouped_w64<NP>), dim3((unsigned)blocks),
                      dim3(64 * moe::down_grouped_waves(NP)),
@@ -332,18 +332,23 @@ DownLaunch pick_down_grouped(int np) {
   return nullptr;
 }
 
-// Variant table (graph-timed sweeps on MI355X, H = 2048 and 4096, 128
-// experts, top-8, uniform routing): the per-token kernel while few tokens
-// share an expert, the expert-grouped one from two slots per expert on.
+// Variant table (graph-timed sweeps on MI355X, 128 experts, top-8, uniform
+// routing): the per-token kernel while few tokens share an expert, the
+// expert-grouped one from two slots per expert on (H = 2048, I = 768: 32
+// tokens 43.5 vs 46.4 us, 16 tokens 29.6 vs 28.5), or from one slot per
+// expert on with two passes over I (H = 4096, I = 1536: 16 tokens 103 vs
+// 115 us, 64 tokens 245 vs 364).
 int down_default_variant(int B, int H, int I, int E, int k) {
   (void)H;
   const long long slots = (long long)B * k;
-  if (slots >= 2LL * E && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
+  const long long need = passes(I) >= 2 ? (long long)E : 2LL * E;
+  if (slots >= need && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
   return MOE_DOWN_PER_TOKEN;
 }
 
 // The launcher for (variant, rows); 0 selects the table's choice.  The
-// grouped kernel always takes 8 rows per wavefront.
+// grouped kernel takes a fixed number of rows per wavefront (8 for I <= 1024,
+// else 4).
 DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, int k) {
   if (variant == 0) variant = down_default_variant(B, H, I, E, k);
   if (variant == MOE_DOWN_PER_TOKEN) {
@@ -352,8 +357,9 @@ DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, in
     return down_allowed(np, rows) ? pick_down(np, rows) : nullptr;
   }
   if (variant == MOE_DOWN_EXPERT_GROUPED) {
-    if (rows == 0) rows = moe::kDownGroupedRows;
-    if (rows != moe::kDownGroupedRows || !down_grouped_allowed(I, (long long)B * k, B, E)) return nullptr;
+    const int ro = moe::down_grouped_rows(passes(I));
+    if (rows == 0) rows = ro;
+    if (rows != ro || !down_grouped_allowed(I, (long long)B * k, B, E)) return nullptr;
     return pick_down_grouped(passes(I));
   }
   return nullptr;

@@ -130,14 +130,14 @@ def test_small_shapes_all_variants(dev, small_layers, shape, rows, variant):
     B, H, I, E, k = shape
     D = small_layers[shape]
     # register-feasible variants only (passes of 1024 elements per lane group);
-    # the grouped down kernel always takes 8 rows
+    # the grouped down kernel takes 8 rows (I <= 1024) or 4
     n_gu, n_dn = -(-H // 1024), -(-(k * I) // 1024)
     cap = 16 if variant == PER_SLOT else 8
     rows_gu = rows if rows is None or rows * n_gu <= cap else None
     if variant == PER_SLOT:
         rows_dn = rows if rows is None or n_dn * (5 * rows + 8) <= 224 else None
     else:
-        rows_dn = rows if rows == 8 else None
+        rows_dn = rows if rows == (8 if I <= 1024 else 4) else None
     x = mi.make_x(7, B, H)
     ids, w = mi.route_uniform(7, B, E, k)
     h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn, variant=variant)
