@@ -11,9 +11,10 @@
 // tokens x 8 of 128 experts, 2.3 times on average).
 //
 // Steps of one workgroup (NW wavefronts):
-//  1. sort the B*k slots by expert in LDS (slot_sort.hpp); each wavefront's
-//     first expert's rows are requested between the two phases of the sort;
-//  2. wavefront w takes the routed experts w, w + NW, ...  For each it loads
+//  1. index the B*k slots by expert in LDS (slot_index.hpp);
+//  2. the slots of each routed expert are cut into work units of at most 8
+//     (so that an expert shared by many tokens is spread over wavefronts);
+//     wavefront w takes the units w, w + NW, ...  For each it loads
 //     the expert's RO rows -- contiguous in memory, read as RO row passes
 //     where lane l takes the 16 bytes at 16 l (+1024 per pass) -- and their
 //     RO x I/32 E8M0 scales with one dword load per lane (moved to the
@@ -25,27 +26,28 @@
 //     wavefront (B <= 64);
 //  3. the NW wavefronts' accumulators meet in LDS and thread (b, r) adds them
 //     in wavefront order and writes y[b, o0 + r] once.
-// Within a wavefront each token's sum runs over experts in ascending order
-// and, within an expert, slots in slot order; across wavefronts in wavefront
-// order: the result does not depend on timing.  Outputs of a token with an
+// Within a wavefront each token's sum runs over its units in order (experts
+// ascending, slots in slot order); across wavefronts in wavefront order: the
+// result does not depend on timing.  Outputs of a token with an
 // invalid id, or touching a row with a NaN scale code, are NaN.
 #pragma once
 
-#include "slot_sort.hpp"
+#include "slot_index.hpp"
 
 namespace moe {
 
 constexpr int kDownGroupedMaxTokens = 64;  // one token per lane
 constexpr int kDownGroupedSlotsPerRound = 2;
+constexpr int kDownGroupedUnitSlots = 8;   // slots per work unit: a hot expert is spread over wavefronts
 
 // Launch shape by passes of 1024 elements over I (graph-timed on MI355X):
 // one pass (I <= 1024): 8 output dimensions per workgroup of 16 wavefronts;
 // two passes: 4 output dimensions per workgroup of 8 wavefronts.
 __host__ __device__ constexpr int down_grouped_rows(int np) { return np <= 1 ? 8 : 4; }
 __host__ __device__ constexpr int down_grouped_waves(int np) { return np <= 1 ? 16 : 8; }
-// LDS layout: slot sort | per-wavefront accumulators [NW][RO][64] floats | NaN masks [NW][64]
+// LDS layout: slot index | per-wavefront accumulators [NW][RO][64] floats | NaN masks [NW][64]
 __host__ __device__ constexpr int down_grouped_lds_bytes(int np, int E, int S) {
-  return slot_sort_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (down_grouped_rows(np) + 1) * 4;
+  return slot_index_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (down_grouped_rows(np) + 1) * 4;
 }
 
 template <int NP>
@@ -63,10 +65,8 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int o0 = blockIdx.x * RO;
-  SlotSorter<NT> sorter;
-  sorter.count(lds, ids, slots, E, k);
-  const SlotSort& so = sorter.o;
-  float* accs = reinterpret_cast<float*>(lds + slot_sort_lds_bytes(E, slots));   // [NW][RO][64]
+  const SlotIndex si = build_slot_index<NT>(lds, ids, slots, E, k, kDownGroupedUnitSlots);
+  float* accs = reinterpret_cast<float*>(lds + slot_index_lds_bytes(E, slots));   // [NW][RO][64]
   uint32_t* nans = reinterpret_cast<uint32_t*>(accs + NW * RO * 64);             // [NW][64]
 
   const int nblk = I >> 5;
@@ -101,18 +101,17 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
 #pragma unroll
       for (int c = 0; c < NP; ++c) wv[r][c] = bload16(wr, off[c], (row0 + r) * (uint32_t)I);
   };
-  // One routed expert with its rows already requested: its slots' h rows,
-  // dot products and accumulation.
-  auto process = [&](int u) {
-    const int e = __builtin_amdgcn_readfirstlane(so.used[u]);
-    const int beg = so.begin(e);
-    const int count = so.end(e) - beg;   // >= 1
+  // One work unit (up to 8 slots of one routed expert) with its expert's rows
+  // already requested: its slots' h rows, dot products and accumulation.
+  auto process = [&](int un) {
+    int e, first, count;   // slots si.sorted[first .. first + count), count 1 .. kDownGroupedUnitSlots
+    si.unit(un, e, first, count);
 
     // h rows and router weights of the first round of slots
     auto load_round = [&](int m0, u32x4 (&hv)[MS][NP][2], float (&ws)[MS]) {
 #pragma unroll
       for (int m = 0; m < MS; ++m) {
-        const uint32_t ent = so.sorted[beg + min(m0 + m, count - 1)];   // past the end: repeat, unused
+        const uint32_t ent = si.sorted[first + min(m0 + m, count - 1)];   // past the end: repeat, unused
         const uint32_t sl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ent & 0xFFFFu));
 #pragma unroll
         for (int c = 0; c < NP; ++c) {
@@ -170,7 +169,7 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
             for (int c = 0; c < NP; ++c) p[r] += apply_e8m0(chunk_dot(wv[r][c], hv[m][c], 0.0f), sc[r][c], bias[c]);
           }
           const float tot = wave_reduce_scatter<RO>(p, lane);
-          const int b = __builtin_amdgcn_readfirstlane((int)(so.sorted[beg + m0 + m] >> 16));
+          const int b = __builtin_amdgcn_readfirstlane((int)(si.sorted[first + m0 + m] >> 16));
           const float wsm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ws[m])));
           const float fw = lane == b ? wsm : 0.0f;   // only token b's lane accumulates
 #pragma unroll
@@ -194,17 +193,15 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
     }
     };
 
-  // The first expert's rows go out before the slots are scattered.  The load
-  // is unconditional (a wavefront without an expert reads one it will not
-  // use) and the first expert is processed outside the loop, so no row
-  // register is merged across a branch or carried around the loop: either
-  // made the compiler wait for the loads before the scatter.
-  load_rows(so.n_used > 0 ? __builtin_amdgcn_readfirstlane(so.used[min(w, so.n_used - 1)]) : 0);
-  sorter.scatter();
-  if (w < so.n_used) process(w);
-  for (int u = w + NW; u < so.n_used; u += NW) {
-    load_rows(__builtin_amdgcn_readfirstlane(so.used[u]));
-    process(u);
+  // The first unit is processed outside the loop and its rows are loaded
+  // unconditionally (a wavefront without a unit reads rows it will not use),
+  // so no row register is merged across a branch or carried around the loop:
+  // either made the compiler wait for the loads right away.
+  load_rows(si.n_units > 0 ? si.unit_expert(min(w, si.n_units - 1)) : 0);
+  if (w < si.n_units) process(w);
+  for (int un = w + NW; un < si.n_units; un += NW) {
+    load_rows(si.unit_expert(un));
+    process(un);
   }
 
   // ---- the wavefronts' partial sums meet in LDS; thread (b, r) adds them in wavefront order
@@ -221,7 +218,7 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
       nn |= nans[v * 64 + b];
     }
     bool nan_out = (nn >> r) & 1u;
-    if (so.n_bad > 0) {   // a token with an invalid id is NaN everywhere
+    if (si.n_bad > 0) {   // a token with an invalid id is NaN everywhere
       for (int j = 0; j < k; ++j) nan_out |= (unsigned)ids[b * k + j] >= (unsigned)E;
     }
     y[(size_t)b * H + o0 + r] = f32_to_bf16_rne(nan_out ? qnan() : sum);

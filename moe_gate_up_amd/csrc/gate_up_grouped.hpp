@@ -13,10 +13,13 @@
 //
 // The grid is persistent: about as many workgroups as the chip holds at once,
 // each taking work items blockIdx.x, blockIdx.x + gridDim.x, ...  Every
-// workgroup first sorts the B*k <= 1024 slots by expert in LDS (a counting
-// sort with LDS atomics; within an expert the slot order is arbitrary and does
-// not affect any output), which yields the routed experts and each one's slot
-// range.  Unrouted experts produce no work items.  Per item:
+// workgroup first indexes the B*k <= 1024 slots by expert in LDS
+// (slot_index.hpp), which yields the routed experts and each one's slots, cut
+// into work units of at most 4M slots (four fillings of the LDS staging area
+// of M x rows), so that an expert shared by many tokens is spread over
+// several workgroups while an expert with a handful of slots is one unit (its
+// rows read once).  Unrouted experts produce no work.  A work item is a work
+// unit times a group of 4R neurons:
 //  1. each wavefront issues its R gate and R up rows (1 KB-contiguous passes
 //     as in the per-slot kernel) and their E8M0 scales;
 //  2. per chunk of up to M slots, the 4 wavefronts copy those tokens' x rows
@@ -31,26 +34,34 @@
 // exactly once.
 #pragma once
 
-#include "slot_sort.hpp"
+#include "slot_index.hpp"
 
 namespace moe {
 
 constexpr int kGroupedMaxSlots = kSortMaxSlots;       // B*k limit of the expert-grouped variant
 constexpr int kGroupedMaxExperts = kSortMaxExperts;   // E limit
 constexpr int kGroupedXBytes = 16384;                 // LDS for staged activations
+constexpr int kGroupedUnitChunks = 4;                 // staging rounds per work unit
 
 // bytes of one staged x row (1 KB-padded) and rows per chunk
 __host__ __device__ constexpr int grouped_xrow(int H) { return ((2 * H + 1023) / 1024) * 1024; }
 __host__ __device__ constexpr int grouped_chunk(int H) {
   return kGroupedXBytes / grouped_xrow(H) < 1 ? 1 : kGroupedXBytes / grouped_xrow(H);
 }
-// LDS layout: slot sort | staged x [M rows]
+// slots per work unit: four fillings of the staging area
+__host__ __device__ constexpr int grouped_unit_slots(int H) { return kGroupedUnitChunks * grouped_chunk(H); }
+// LDS layout: slot index | staged x [M rows]
 __host__ __device__ constexpr int grouped_lds_bytes(int E, int S, int H) {
-  return slot_sort_lds_bytes(E, S) + grouped_chunk(H) * grouped_xrow(H);
+  return slot_index_lds_bytes(E, S) + grouped_chunk(H) * grouped_xrow(H);
 }
 
+// Up to 4 rows x passes: at least 4 wavefronts per SIMD (<= 128 VGPRs), so
+// that the persistent grid keeps 4 workgroups per CU in flight.
+__host__ __device__ constexpr int grouped_min_waves(int nch, int r) { return nch * r <= 4 ? 4 : 1; }
+
 template <int NCH, int R>
-__global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(grouped_min_waves(NCH, R))))
+void moe_gate_up_expert_grouped_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
     const uint8_t* __restrict__ wu, const uint8_t* __restrict__ su,
@@ -60,11 +71,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  SlotSorter<256> sorter;
-  sorter.count(lds, ids, slots, E, k);
-  sorter.scatter();
-  const SlotSort& so = sorter.o;
-  uint8_t* xs = lds + slot_sort_lds_bytes(E, slots);   // M rows of x, 2H bytes each, 1 KB-padded
+  const SlotIndex si = build_slot_index<256>(lds, ids, slots, E, k, grouped_unit_slots(H));
+  uint8_t* xs = lds + slot_index_lds_bytes(E, slots);   // M rows of x, 2H bytes each, 1 KB-padded
   const rsrc_t idr = make_rsrc(ids, (uint64_t)slots * 4);
 
   // ---- per-lane constants of the R-row passes
@@ -88,9 +96,9 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   const int pieces = XS >> 10;
   const int M = grouped_chunk(H);
 
-  // ---- work items: (routed expert u, group of 4 tiles g)
+  // ---- work items: (work unit = up to M slots of one routed expert, group of 4 tiles g)
   const int n_grp = (I + 4 * R - 1) / (4 * R);
-  const int n_items = so.n_used * n_grp;
+  const int n_items = si.n_units * n_grp;
   u32x4 gw[R][NCH], uw[R][NCH];
   uint32_t gsc[R][NCH], usc[R][NCH];
   auto load_rows = [&](int e, int n0) {   // the wavefront's R gate and R up rows of expert e
@@ -107,17 +115,16 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
       }
     }
   };
-  auto item_expert = [&](int item, int& e, int& n0) {
-    const int u = __builtin_amdgcn_readfirstlane(item / n_grp);   // VALU division, uniform result
-    e = __builtin_amdgcn_readfirstlane(so.used[u]);
-    n0 = ((item - u * n_grp) * 4 + w) * R;   // this wavefront's first neuron (may be >= I: nothing stored)
+  // the item's expert, its unit's slots (si.sorted[first .. first + count)) and the wavefront's first neuron
+  auto item_unit = [&](int item, int& e, int& first, int& count, int& n0) {
+    const int un = __builtin_amdgcn_readfirstlane(item / n_grp);   // VALU division, uniform result
+    si.unit(un, e, first, count);
+    n0 = ((item - un * n_grp) * 4 + w) * R;   // may be >= I: nothing stored
   };
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    int e, n0;
-    item_expert(item, e, n0);
+    int e, first, count, n0;   // count: 1 .. 4M
+    item_unit(item, e, first, count, n0);
     load_rows(e, n0);
-    const int beg = so.begin(e);
-    const int count = so.end(e) - beg;   // >= 1
 
     // x rows are copied global -> LDS without passing through registers
     // (buffer loads with the LDS bit: lane l's 16 bytes land at the
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
       const int nm = min(M, count - m0);
       for (int m = 0; m < nm; ++m) {
         const uint32_t xo =
-            (uint32_t)__builtin_amdgcn_readfirstlane((int)(so.sorted[beg + m0 + m] >> 16)) * (uint32_t)H * 2u;
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(si.sorted[first + m0 + m] >> 16)) * (uint32_t)H * 2u;
         for (int p = w; p < pieces; p += 4)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xs + m * XS + 1024 * p),
                                                    16, xo + 1024u * p + 16u * lane, 0, 0, 0);
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
         nan_out = r_out >= 0 && ((nan_rows >> r_out) & 1);
       }
       for (int m = 0; m < nm; ++m) {
-        const int s = (int)(so.sorted[beg + m0 + m] & 0xFFFFu);
+        const int s = (int)(si.sorted[first + m0 + m] & 0xFFFFu);
         u32x4 xa[NCH][2];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_expert_grouped_w64(
   }
 
   // ---- slots with an invalid expert id: NaN in every neuron
-  if (so.n_bad > 0) {
+  if (si.n_bad > 0) {
     for (int sl = blockIdx.x; sl < slots; sl += gridDim.x) {
       const int v = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(idr, (uint32_t)sl * 4u, 0, 0));
       if ((unsigned)__builtin_amdgcn_readfirstlane(v) >= (unsigned)E)

@@ -139,8 +139,8 @@ template <int NCH, int R>
 long long launch_grouped_t(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
                            const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
                            int k) {
-  const long long slots = (long long)B * k;
-  const long long items_max = (E < slots ? E : slots) * (long long)((I + 4 * R - 1) / (4 * R));
+  const long long slots = (long long)B * k;   // work units (<= slots) x groups of 4 tiles
+  const long long items_max = slots * (long long)((I + 4 * R - 1) / (4 * R));
   const long long blocks = items_max < kGroupedBlocks ? items_max : kGroupedBlocks;
   if (!go) return blocks;
   hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
