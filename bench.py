@@ -13,7 +13,9 @@ activations, routing, the intermediate's write and read, and the output
 (layer_bytes below).  Also reported: microseconds per layer, the fraction of a
 copy-kernel peak measured in the same process (the efficiency figure of the
 blog post's "Hardware efficiency" section), a B sweep, the dominant kernel's
-roofline position, and the CPU oracle timed on the host as a baseline.
+roofline position, the conventional expert-centric path timed on the same
+batches (the blog post's "Stage elimination" A/B), and the CPU oracle timed
+on the host as a baseline.
 
 Weights: one layer is generated on the host (seed 0) and uploaded into
 `--copies` separate device buffers; step i uses copy i mod copies, so
@@ -176,7 +178,8 @@ def main():
             info.append(layer_bytes(ids, H_, I_, k_))
         return (up(np.stack(xs)), up(np.stack(ids_l)), up(np.stack(ws)), info)
 
-    def run_steps(wcopies, shape, B, steps, warmup, n_rout, kind="uniform", seed=None, layers=1, kernels=True):
+    def run_steps(wcopies, shape, B, steps, warmup, n_rout, kind="uniform", seed=None, layers=1, kernels=True,
+                  path="warp"):
         """Time `steps` steps; a step is `layers` whole-layer passes (both kernels),
         layer l of a step reading weight copy l (cycled) with its own routing.
         Then each kernel alone in a back-to-back loop of steps*layers launches.
@@ -201,7 +204,16 @@ def main():
             r = i % n_rout
             mg.moe_decode_down(h, idss[r], wss[r], wd, sd, y)
 
+        ws = None
+        if path == "conventional":   # the expert-centric A/B path: seven launches through a workspace
+            ws = torch.empty(mg.moe_decode_conventional_workspace(B, H_, I_, E_, k_), dtype=torch.uint8, device=dev)
+
         def layer(i):
+            if ws is not None:
+                wg, sg, wu, su, wd, sd = wcopies[i % len(wcopies)]
+                r = i % n_rout
+                mg.moe_decode_conventional(xs[r], idss[r], wss[r], wg, sg, wu, su, wd, sd, y, ws)
+                return
             gate_up(i)
             down(i)
 
@@ -275,6 +287,20 @@ def main():
             log(f"routing {kind} B=32: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s "
                 f"({r['frac_of_copy_peak']:.1%}), {r['distinct_experts']:.1f} distinct experts")
         extra["routing_stress_b32"] = c3
+
+        # A/B: the conventional expert-centric path (route, pad, quantise, scatter, per-expert
+        # buffers, combine: seven launches) on the same weights, routings and batches
+        ab = []
+        warp = {r["B"]: r for r in sweep}
+        for b in (1, 8, 32):
+            rw = warp.get(b) or brief(run_steps(copies, S1, b, args.sweep_steps, 10, args.routings, kernels=False))
+            rc = run_steps(copies, S1, b, args.sweep_steps, 10, args.routings, kernels=False, path="conventional")
+            ab.append({"B": b, "warp_decode_us_per_layer": round(rw["us_per_layer"], 3),
+                       "conventional_us_per_layer": round(rc["us_per_layer"], 3),
+                       "speedup": round(rc["us_per_layer"] / rw["us_per_layer"], 3)})
+            log(f"conventional path B={b}: {rc['us_per_layer']:.2f} us/layer vs warp decode "
+                f"{rw['us_per_layer']:.2f} us ({rc['us_per_layer'] / rw['us_per_layer']:.2f}x)")
+        extra["conventional_ab"] = ab
 
         # 48-layer decode step: 48 weight copies at distinct addresses, fresh routing per layer
         deep = [copies[i % len(copies)] if i < len(copies) else [t.clone() for t in first] for i in range(48)]

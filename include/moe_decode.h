@@ -155,6 +155,31 @@ int moe_decode_down_ex(const void *h, const int32_t *topk_ids, const float *topk
 int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int *variant, int *rows_per_wave, int *workgroups);
 int moe_decode_down_plan(int B, int H, int I, int E, int k, int *variant, int *rows_per_wave, int *workgroups);
 
+/* The conventional, expert-centric path, for A/B comparison (blog post,
+ * sections "The traditional MoE path", "Stage elimination", "Eliminating
+ * buffers" and "Accuracy improvement").  Same layer as gate_up + down, but
+ * computed the way an expert-centric pipeline does it, as seven launches on
+ * `stream` through caller-provided device workspace: route (per-expert token
+ * lists, each padded to a power of two), quantise x to MXFP8 (E4M3 codes and
+ * one E8M0 scale 2^(floor(log2 amax) - 8) per 32 along H, saturating at 448),
+ * scatter the quantised rows into an expert-major gather buffer, gate/up per
+ * row (h = bf16(SiLU(G) * U)), quantise h to MXFP8 (blocks along I), down per
+ * row into a bf16 per-expert output buffer, and the weighted combine y[b] =
+ * bf16(sum_j w[b,j] * out[b,j]).  Padding rows are computed and discarded.
+ * Inputs and y as for the two calls above; `workspace` is device memory of at
+ * least the size moe_decode_conventional_workspace() reports, 256-byte
+ * aligned, owned by the caller, disjoint from every input and from y, and
+ * used only until the launches complete.  Limits: B*k <= 1024, E <= 1024,
+ * H and I <= 8192.  Returns MOE_ERR_ARG if the workspace is too small;
+ * otherwise the error codes above. */
+int moe_decode_conventional_workspace(int B, int H, int I, int E, int k, size_t *bytes);
+int moe_decode_conventional(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                            const uint8_t *w_gate, const uint8_t *s_gate,
+                            const uint8_t *w_up, const uint8_t *s_up,
+                            const uint8_t *w_down, const uint8_t *s_down,
+                            void *y_out, void *workspace, size_t workspace_bytes,
+                            int B, int H, int I, int E, int k, void *stream);
+
 /* Bandwidth probes that set the denominator of the efficiency figure (blog
  * post, "Hardware efficiency": peak measured with a copy kernel over
  * contiguous memory).  copy: dst[0:bytes) = src[0:bytes); read: reads

@@ -32,7 +32,8 @@ MOE_DOWN_EXPERT_GROUPED = 2
 
 EXPORTS = (
     "moe_decode_gate_up", "moe_decode_down", "moe_decode_gate_up_ex", "moe_decode_down_ex",
-    "moe_decode_gate_up_plan", "moe_decode_down_plan", "moe_decode_copy_peak", "moe_decode_read_peak",
+    "moe_decode_gate_up_plan", "moe_decode_down_plan", "moe_decode_conventional_workspace",
+    "moe_decode_conventional", "moe_decode_copy_peak", "moe_decode_read_peak",
     "moe_decode_strerror",
 )
 
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
             L.moe_decode_down_ex.argtypes = [P] * 6 + [I] * 7 + [P]
             L.moe_decode_gate_up_plan.argtypes = [I] * 5 + [IP, IP, IP]
             L.moe_decode_down_plan.argtypes = [I] * 5 + [IP, IP, IP]
+            L.moe_decode_conventional_workspace.argtypes = [I] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+            L.moe_decode_conventional.argtypes = [P] * 11 + [S] + [I] * 5 + [P]
             L.moe_decode_copy_peak.argtypes = [P, P, S, P]
             L.moe_decode_read_peak.argtypes = [P, S, P, P]
             L.moe_decode_strerror.argtypes = [I]
@@ -169,6 +172,38 @@ def moe_decode_down_plan(B, H, I, E, k):
     if rc:
         raise MoeDecodeError(rc, "moe_decode_down_plan")
     return v.value, r.value, g.value
+
+
+def moe_decode_conventional_workspace(B, H, I, E, k):
+    """Bytes of device workspace moe_decode_conventional needs."""
+    n = ctypes.c_size_t()
+    rc = lib().moe_decode_conventional_workspace(B, H, I, E, k, ctypes.byref(n))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_conventional_workspace")
+    return n.value
+
+
+def moe_decode_conventional(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y_out, workspace,
+                            stream=None):
+    """The expert-centric path (see include/moe_decode.h); workspace: a uint8 GPU tensor."""
+    T = _types()
+    B, H = x.shape
+    k = topk_ids.shape[-1]
+    E, I = w_gate.shape[0], w_gate.shape[1]
+    wb = E * I * H
+    args = [
+        _dev(x, "x", B * H, T["bf16"]), _dev(topk_ids, "topk_ids", B * k, T["i32"]),
+        _dev(topk_weights, "topk_weights", B * k, T["f32"]),
+        _dev(w_gate, "w_gate", wb, T["u8"]), _dev(s_gate, "s_gate", wb // 32, T["u8"]),
+        _dev(w_up, "w_up", wb, T["u8"]), _dev(s_up, "s_up", wb // 32, T["u8"]),
+        _dev(w_down, "w_down", wb, T["u8"]), _dev(s_down, "s_down", wb // 32, T["u8"]),
+        _dev(y_out, "y_out", B * H, T["bf16"]), _dev(workspace, "workspace", None, T["u8"]),
+        workspace.numel(), B, H, I, E, k,
+    ]
+    rc = lib().moe_decode_conventional(*args, _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_conventional")
+    return y_out
 
 
 def moe_decode_copy_peak(src, dst, stream=None):

@@ -8,6 +8,7 @@
 #include "moe_decode.h"
 #include "down.hpp"
 #include "down_grouped.hpp"
+#include "conventional.hpp"
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
 #include "peak.hpp"
@@ -384,6 +385,105 @@ int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t*
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------- conventional path
+// Workspace layout (every part 256-byte aligned).
+struct ConvLayout {
+  size_t meta, row_slot, row_expert, slot_row, xq, xs, xg, xgs, hb, hq, hs, ob, total;
+  ConvLayout(int B, int H, int I, int E, int k) {
+    const size_t S = (size_t)B * k, P = 2 * S;
+    size_t o = 0;
+    auto take = [&](size_t n) { const size_t r = o; o += (n + 255) & ~(size_t)255; return r; };
+    meta = take(4 * (3 * (size_t)E + 1));
+    row_slot = take(4 * P);
+    row_expert = take(4 * P);
+    slot_row = take(4 * S);
+    xq = take((size_t)B * H);
+    xs = take((size_t)B * H / 32);
+    xg = take(P * H);
+    xgs = take(P * H / 32);
+    hb = take(P * I * 2);
+    hq = take(P * I);
+    hs = take(P * I / 32);
+    ob = take(P * H * 2);
+    total = o;
+  }
+};
+
+constexpr int kConvMaxPasses = 8;   // H and I up to 8192
+
+using ConvGemv = void (*)(dim3, hipStream_t, const uint8_t*, const uint8_t*, const int*, const int*, const uint8_t*,
+                          const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*, int, int, int, int, int);
+
+template <int NP, bool SWIGLU>
+void launch_conv_gemv_t(dim3 grid, hipStream_t st, const uint8_t* aq, const uint8_t* as, const int* row_expert,
+                        const int* meta, const uint8_t* w0, const uint8_t* s0, const uint8_t* w1, const uint8_t* s1,
+                        uint16_t* out, int E, int N, int K, int Pmax, int tiles) {
+  constexpr int R = SWIGLU ? (NP <= 2 ? 2 : 1) : (NP <= 2 ? 4 : (NP <= 4 ? 2 : 1));
+  hipLaunchKernelGGL((moe::conv_gemv_kernel<NP, R, SWIGLU>), grid, dim3(64 * kWavesPerBlock), 0, st, aq, as, row_expert,
+                     meta, w0, s0, w1, s1, out, E, N, K, Pmax, tiles);
+}
+constexpr int conv_rows(int np, bool swiglu) { return swiglu ? (np <= 2 ? 2 : 1) : (np <= 2 ? 4 : (np <= 4 ? 2 : 1)); }
+
+template <bool SWIGLU, int... NPs>
+ConvGemv pick_conv_np(int np, std::integer_sequence<int, NPs...>) {
+  ConvGemv fn = nullptr;
+  ((np == NPs + 1 ? (fn = launch_conv_gemv_t<NPs + 1, SWIGLU>, 0) : 0), ...);
+  return fn;
+}
+
+int conventional_impl(const void* x, const int32_t* ids, const float* tw, const uint8_t* wg, const uint8_t* sg,
+                      const uint8_t* wu, const uint8_t* su, const uint8_t* wd, const uint8_t* sd, void* y, void* ws,
+                      size_t ws_bytes, int B, int H, int I, int E, int k, void* stream) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if ((long long)B * k > moe::kConvMaxSlots || E > moe::kConvMaxSlots || passes(H) > kConvMaxPasses ||
+      passes(I) > kConvMaxPasses)
+    return MOE_ERR_SHAPE;
+  if (B == 0) return MOE_OK;
+  if (!x || !ids || !tw || !wg || !sg || !wu || !su || !wd || !sd || !y || !ws) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(y, 2) ||
+      !aligned(ids, 4) || !aligned(tw, 4) || !aligned(ws, 256))
+    return MOE_ERR_ALIGN;
+  const ConvLayout L(B, H, I, E, k);
+  if (ws_bytes < L.total) return MOE_ERR_ARG;
+  const size_t yb = (size_t)B * H * 2, wb = (size_t)E * I * H;
+  const void* ins[] = {x, ids, tw, wg, sg, wu, su, wd, sd};
+  const size_t insz[] = {(size_t)B * H * 2, (size_t)B * k * 4, (size_t)B * k * 4, wb, wb / 32, wb, wb / 32, wb, wb / 32};
+  for (int i = 0; i < 9; ++i)
+    if (overlaps(y, yb, ins[i], insz[i]) || overlaps(ws, L.total, ins[i], insz[i])) return MOE_ERR_ALIAS;
+  if (overlaps(y, yb, ws, L.total)) return MOE_ERR_ALIAS;
+  ConvGemv gu = pick_conv_np<true>(passes(H), std::make_integer_sequence<int, kConvMaxPasses>{});
+  ConvGemv dn = pick_conv_np<false>(passes(I), std::make_integer_sequence<int, kConvMaxPasses>{});
+  if (!gu || !dn) return MOE_ERR_SHAPE;
+
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  int* meta = reinterpret_cast<int*>(w8 + L.meta);
+  int* row_slot = reinterpret_cast<int*>(w8 + L.row_slot);
+  int* row_expert = reinterpret_cast<int*>(w8 + L.row_expert);
+  int* slot_row = reinterpret_cast<int*>(w8 + L.slot_row);
+  const int S = B * k, Pmax = 2 * S;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto blocks = [](long long n) { return dim3((unsigned)((n + 255) / 256)); };
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(moe::conv_route_kernel, dim3(1), dim3(1024), 0, st, ids, S, E, Pmax, meta, row_slot, row_expert,
+                     slot_row);
+  hipLaunchKernelGGL(moe::conv_quant_kernel, blocks((long long)B * (H / 32)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), B, H, nullptr, w8 + L.xq, w8 + L.xs);
+  hipLaunchKernelGGL(moe::conv_scatter_kernel, blocks((long long)Pmax * (H / 16 + H / 32)), dim3(256), 0, st,
+                     w8 + L.xq, w8 + L.xs, row_slot, meta, E, Pmax, H, k, w8 + L.xg, w8 + L.xgs);
+  const int rg = conv_rows(passes(H), true), tg = (I + rg - 1) / rg;
+  gu(dim3((unsigned)(((long long)tg * Pmax + kWavesPerBlock - 1) / kWavesPerBlock)), st, w8 + L.xg, w8 + L.xgs,
+     row_expert, meta, wg, sg, wu, su, reinterpret_cast<uint16_t*>(w8 + L.hb), E, I, H, Pmax, tg);
+  hipLaunchKernelGGL(moe::conv_quant_kernel, blocks((long long)Pmax * (I / 32)), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(w8 + L.hb), Pmax, I, meta + 3 * E, w8 + L.hq, w8 + L.hs);
+  const int rd = conv_rows(passes(I), false), td = (H + rd - 1) / rd;
+  dn(dim3((unsigned)(((long long)td * Pmax + kWavesPerBlock - 1) / kWavesPerBlock)), st, w8 + L.hq, w8 + L.hs,
+     row_expert, meta, wd, sd, nullptr, nullptr, reinterpret_cast<uint16_t*>(w8 + L.ob), E, H, I, Pmax, td);
+  hipLaunchKernelGGL(moe::conv_combine_kernel, blocks((long long)B * H), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(w8 + L.ob), slot_row, tw, static_cast<uint16_t*>(y), B, H, k);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +511,22 @@ int moe_decode_down_ex(const void* h, const int32_t* topk_ids, const float* topk
                        int rows_per_wave, void* stream) {
   if (rows_per_wave < 0 || variant < 0) return MOE_ERR_ARG;
   return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, variant, rows_per_wave, stream);
+}
+
+int moe_decode_conventional_workspace(int B, int H, int I, int E, int k, size_t* bytes) {
+  int rc = check_shape(B, H, I, E, k);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = ConvLayout(B, H, I, E, k).total;
+  return MOE_OK;
+}
+
+int moe_decode_conventional(const void* x, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_gate,
+                            const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                            const uint8_t* s_down, void* y_out, void* workspace, size_t workspace_bytes, int B, int H,
+                            int I, int E, int k, void* stream) {
+  return conventional_impl(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y_out, workspace,
+                           workspace_bytes, B, H, I, E, k, stream);
 }
 
 int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int* rows_per_wave, int* workgroups) {

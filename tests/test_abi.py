@@ -129,6 +129,29 @@ def test_bad_tuning_arguments():
     assert dn(E=1025, rows=0, variant=G) == mg.MOE_ERR_ARG        # E > 1024
 
 
+def cv(x=A, ids=A + 1 * S, tw=A + 2 * S, wg=A + 3 * S, sg=A + 4 * S, wu=A + 5 * S, su=A + 6 * S, wd=A + 7 * S,
+       sd=A + 8 * S, y=A + 9 * S, ws=A + 10 * S, ws_bytes=1 << 30, B=2, H=2048, I=768, E=128, k=8):
+    L = mg.lib()
+    args = [ctypes.c_void_p(p) for p in (x, ids, tw, wg, sg, wu, su, wd, sd, y, ws)]
+    return L.moe_decode_conventional(*args, ctypes.c_size_t(ws_bytes), B, H, I, E, k, None)
+
+
+def test_conventional_path_arguments():
+    need = mg.moe_decode_conventional_workspace(2, 2048, 768, 128, 8)
+    assert 0 < need < (1 << 30)
+    # grows with the batch: the padded rows are at most twice the slots
+    assert mg.moe_decode_conventional_workspace(32, 2048, 768, 128, 8) > 8 * need
+    assert cv(B=0) == mg.MOE_OK
+    assert cv(ws=0) == mg.MOE_ERR_NULL
+    assert cv(ws=A + 10 * S + 16) == mg.MOE_ERR_ALIGN          # workspace must be 256-byte aligned
+    assert cv(ws_bytes=need - 1) == mg.MOE_ERR_ARG
+    assert cv(B=129) == mg.MOE_ERR_SHAPE                       # B*k > 1024
+    assert cv(H=16384, I=32) == mg.MOE_ERR_SHAPE               # H beyond 8192
+    assert cv(y=A + 64) == mg.MOE_ERR_ALIAS                    # y overlapping x
+    assert cv(ws=A + 9 * S) == mg.MOE_ERR_ALIAS                # workspace overlapping y
+    assert cv(ws=A + 3 * S + 4096) == mg.MOE_ERR_ALIAS         # workspace overlapping the gate weights
+
+
 def test_plans():
     for B in (1, 8, 16, 32, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
@@ -137,7 +160,7 @@ def test_plans():
             assert g == -(-((768 + r - 1) // r) * B * 8 // 4)
         else:                              # persistent: <= 2048 workgroups, <= the possible work items
             assert v == mg.MOE_GATE_UP_EXPERT_GROUPED
-            assert g == min(2048, min(128, B * 8) * -(-768 // (4 * r)))
+            assert g == min(2048, B * 8 * -(-768 // (4 * r)))
         # grouped once the batch averages two or more slots per expert
         assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
