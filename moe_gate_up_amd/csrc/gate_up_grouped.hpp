@@ -150,7 +150,7 @@ void moe_gate_up_expert_grouped_w64(
         stage(m0);
       }
       const int nm = min(M, count - m0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's copies are in LDS
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wavefront's copies are in LDS
       __syncthreads();
       if (m0 == 0) {   // the scales have arrived by now
         uint64_t nan_rows = 0;   // bit r: an E8M0 NaN code in row r

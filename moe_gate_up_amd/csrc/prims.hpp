@@ -49,6 +49,10 @@ __device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t sof
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
+// s_waitcnt immediate that waits until at most n (< 64) vector-memory
+// operations of the wave are outstanding, leaving the other counters alone.
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
 // E4M3 bytes 0,1 (hi=false) or 2,3 (hi=true) of `word` -> bf16 pair (exact).
 __device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t word, bool hi) {
   return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true)
