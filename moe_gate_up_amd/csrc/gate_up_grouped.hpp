@@ -43,10 +43,13 @@ constexpr int kGroupedMaxExperts = kSortMaxExperts;   // E limit
 constexpr int kGroupedXBytes = 16384;                 // LDS for staged activations
 constexpr int kGroupedUnitChunks = 4;                 // staging rounds per work unit
 
-// bytes of one staged x row (1 KB-padded) and rows per chunk
+// bytes of one staged x row (1 KB-padded) and rows per chunk (at most 8)
+constexpr int kGroupedMaxChunk = 8;
 __host__ __device__ constexpr int grouped_xrow(int H) { return ((2 * H + 1023) / 1024) * 1024; }
 __host__ __device__ constexpr int grouped_chunk(int H) {
-  return kGroupedXBytes / grouped_xrow(H) < 1 ? 1 : kGroupedXBytes / grouped_xrow(H);
+  return kGroupedXBytes / grouped_xrow(H) < 1
+             ? 1
+             : (kGroupedXBytes / grouped_xrow(H) > kGroupedMaxChunk ? kGroupedMaxChunk : kGroupedXBytes / grouped_xrow(H));
 }
 // slots per work unit: four fillings of the staging area
 __host__ __device__ constexpr int grouped_unit_slots(int H) { return kGroupedUnitChunks * grouped_chunk(H); }
@@ -94,7 +97,10 @@ void moe_gate_up_expert_grouped_w64(
   for (int r = 0; r < R; ++r) r_out = (lane == scatter_lane<2 * R>(r)) ? r : r_out;
   const int XS = grouped_xrow(H);
   const int pieces = XS >> 10;
-  const int M = grouped_chunk(H);
+  // x rows per chunk.  MCAP bounds it for this NCH (H > 1024 (NCH - 1), so a
+  // staged row is more than 2 KB (NCH - 1)) and sizes the token registers.
+  constexpr int MCAP = NCH == 1 ? kGroupedMaxChunk : (8 / (NCH - 1) > 0 ? 8 / (NCH - 1) : 1);
+  const int M = min(grouped_chunk(H), MCAP);
 
   // ---- work items: (work unit = up to M slots of one routed expert, group of 4 tiles g)
   const int n_grp = (I + 4 * R - 1) / (4 * R);
@@ -134,12 +140,18 @@ void moe_gate_up_expert_grouped_w64(
     // the lane offset, so reads past the end of x are range-checked (zero).
     auto stage = [&](int m0) {
       const int nm = min(M, count - m0);
-      for (int m = 0; m < nm; ++m) {
-        const uint32_t xo =
-            (uint32_t)__builtin_amdgcn_readfirstlane((int)(si.sorted[first + m0 + m] >> 16)) * (uint32_t)H * 2u;
-        for (int p = w; p < pieces; p += 4)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xs + m * XS + 1024 * p),
-                                                   16, xo + 1024u * p + 16u * lane, 0, 0, 0);
+      uint32_t tok[MCAP];   // the chunk's tokens: all LDS reads first, one round trip
+#pragma unroll
+      for (int m = 0; m < MCAP; ++m)
+        tok[m] = m < nm ? si.sorted[first + m0 + m] >> 16 : 0u;
+#pragma unroll
+      for (int m = 0; m < MCAP; ++m) {
+        if (m < nm) {
+          const uint32_t xo = (uint32_t)__builtin_amdgcn_readfirstlane((int)tok[m]) * (uint32_t)H * 2u;
+          for (int p = w; p < pieces; p += 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xs + m * XS + 1024 * p),
+                                                     16, xo + 1024u * p + 16u * lane, 0, 0, 0);
+        }
       }
     };
     stage(0);   // the first chunk's copies go out before anything waits for the weights

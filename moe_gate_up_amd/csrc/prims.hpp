@@ -96,6 +96,24 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (lane l gets the sum of lanes 0..l):
+// row_shr steps inside each 16-lane row, then row_bcast:15 / row_bcast:31 carry
+// the rows' totals forward.  No LDS.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dppi<0x111>(v);        // row_shr:1
+  v += dppi<0x112>(v);        // row_shr:2
+  v += dppi<0x114>(v);        // row_shr:4
+  v += dppi<0x118>(v);        // row_shr:8
+  v += dppi<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dppi<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Sum over the 16 lanes of each DPP row; every lane of the row gets the row sum.
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1

@@ -31,24 +31,20 @@ struct SlotIndex {
   int* end_;         // end of expert e's range in `sorted` (its start is end_[e - 1], 0 for e = 0)
   int* used;         // routed experts, ascending
   uint32_t* sorted;  // slot | token << 16, grouped by expert, slot order within an expert
-  uint32_t* units;   // work units: routed-expert index u << 16 | chunk i (slots i*ch .. of expert used[u])
+  uint32_t* units;   // work units: expert | first << 10 | count << 21 (its slots are sorted[first .. first + count))
   int n_used;        // routed experts
   int n_units;       // sum over routed experts of ceil(count / ch)
   int n_bad;         // slots whose id is outside [0, E)
   int ch;            // slots per work unit
 
-  __device__ int begin(int e) const { return e > 0 ? __builtin_amdgcn_readfirstlane(end_[e - 1]) : 0; }
-  __device__ int end(int e) const { return __builtin_amdgcn_readfirstlane(end_[e]); }
   // expert of work unit n
-  __device__ int unit_expert(int n) const {
-    return __builtin_amdgcn_readfirstlane(used[__builtin_amdgcn_readfirstlane((int)units[n]) >> 16]);
-  }
+  __device__ int unit_expert(int n) const { return __builtin_amdgcn_readfirstlane((int)(units[n] & 0x3FFu)); }
   // work unit n: its expert, the position of its first slot in `sorted`, and its slot count (1 .. ch)
   __device__ void unit(int n, int& e, int& first, int& count) const {
-    const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)units[n]);
-    e = __builtin_amdgcn_readfirstlane(used[v >> 16]);
-    first = begin(e) + (int)(v & 0xFFFFu) * ch;
-    count = min(ch, end(e) - first);
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)units[n]);   // one LDS read
+    e = (int)(v & 0x3FFu);
+    first = (int)((v >> 10) & 0x7FFu);
+    count = (int)(v >> 21);
   }
 };
 
@@ -94,23 +90,19 @@ __device__ SlotIndex build_slot_index(uint8_t* lds, const int32_t* __restrict__ 
       const int e = e0 + lane;
       const int c = e < E ? o.end_[e] : 0;
       const int nc = (c + ch - 1) / ch;   // work units of expert e
-      int incl = c, uincl = nc;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d), tu = __shfl_up(uincl, d);
-        incl += lane >= d ? t : 0;
-        uincl += lane >= d ? tu : 0;
-      }
-      if (e < E) o.end_[e] = carry + incl - c;   // start, for now
+      const int incl = wave_incl_scan(c), uincl = wave_incl_scan(nc);
+      const int start = carry + incl - c;
+      if (e < E) o.end_[e] = start;   // start, for now
       const uint64_t m = __builtin_amdgcn_ballot_w64(c > 0);
       if (c > 0) {
-        const int u = nu + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        o.used[u] = e;
-        for (int i = 0; i < nc; ++i) o.units[nun + uincl - nc + i] = ((uint32_t)u << 16) | (uint32_t)i;
+        o.used[nu + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = e;
+        for (int i = 0; i < nc; ++i)
+          o.units[nun + uincl - nc + i] =
+              (uint32_t)e | ((uint32_t)(start + i * ch) << 10) | ((uint32_t)min(ch, c - i * ch) << 21);
       }
       nu += __builtin_popcountll(m);
-      carry += __shfl(incl, 63);
-      nun += __shfl(uincl, 63);
+      carry += __builtin_amdgcn_readlane(incl, 63);
+      nun += __builtin_amdgcn_readlane(uincl, 63);
     }
     if (lane == 0) {
       misc[0] = nu;
