@@ -66,8 +66,10 @@ def layer_bytes(ids: np.ndarray, H: int, I: int, k: int) -> dict:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gate_up.hpp", "gate_up_grouped.hpp", "down.hpp", "prims.hpp", "moe_decode.hip"):
-        h.update(open(os.path.join(ROOT, "moe_gate_up_amd", "csrc", f), "rb").read())
+    d = os.path.join(ROOT, "moe_gate_up_amd", "csrc")
+    for f in sorted(os.listdir(d)):   # every kernel source and header of the library
+        if f.endswith((".hpp", ".hip")):
+            h.update(f.encode() + b"\0" + open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
