@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     make_layer,
     make_x,
     route_uniform,
+    router_logits,
     route_zipf,
     route_adversarial,
     route_contiguous,

@@ -194,10 +194,15 @@ def _softmax_f32(logits: np.ndarray) -> np.ndarray:
     return p.astype(np.float32)
 
 
+def router_logits(seed: int, B: int, E: int, it: int = 0) -> np.ndarray:
+    """Router logits ~ N(0,1), FP32 [B,E] (the draw behind route_uniform)."""
+    return _rng(seed, _P_ROUTE, it).standard_normal((B, E), dtype=np.float32)
+
+
 def route_uniform(seed: int, B: int, E: int, k: int, it: int = 0):
     """Router logits ~ N(0,1) [B,E]; ids = top-k by descending logit (ties -> lower id);
     weights = softmax over the k selected logits (= softmax over E renormalised over the top-k)."""
-    logits = _rng(seed, _P_ROUTE, it).standard_normal((B, E), dtype=np.float32)
+    logits = router_logits(seed, B, E, it)
     ids = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
     w = _softmax_f32(np.take_along_axis(logits, ids.astype(np.int64), axis=1))
     return np.ascontiguousarray(ids), np.ascontiguousarray(w)

@@ -7,6 +7,8 @@ this package.  It shares no code with the HIP library and never imports it.
   plain FP64 definition of the layer; this module wraps it with ctypes.
 * ``brute.py`` is an independent pure-Python restatement with exact rational
   arithmetic, used to pin the C code on tiny shapes.
+* ``route`` is the top-k router step in front of the layer (``orc_route`` in
+  the C code), kept to check the router prologue of the HIP library.
 * ``truth_layer`` evaluates the layer with the *unquantised* FP32 weight draws
   and no rounding anywhere (the "full precision" reference of the accuracy
   claim), with NumPy matrix products in FP64.
@@ -53,6 +55,7 @@ def _bind(lib):
     lib.orc_down_at.argtypes = [P, P, P, P, P, P, L, P, i, i, i, i, i]; lib.orc_down_at.restype = i
     lib.orc_conventional.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i, i, i, i, i]; lib.orc_conventional.restype = i
     lib.orc_mx_fake_quant.argtypes = [P, L]; lib.orc_mx_fake_quant.restype = None
+    lib.orc_route.argtypes = [P, P, P, i, i, i]; lib.orc_route.restype = i
     return lib
 
 
@@ -204,6 +207,18 @@ def mx_fake_quant(v):
     a = np.array(v, dtype=np.float64, copy=True).ravel()
     load().orc_mx_fake_quant(_p(a), a.size)
     return a.reshape(np.shape(v))
+
+
+def route(logits, k):
+    """Router step in front of the layer (reading in ``moe_oracle.c``, ``orc_route``):
+    logits FP32 [B,E] -> (ids int32 [B,k], largest logit first, lower id first among
+    equal logits; weights FP64 [B,k] = softmax over E renormalised over the k)."""
+    logits = _c(logits, np.float32)
+    B, E = logits.shape
+    ids = np.empty((B, k), np.int32)
+    w = np.empty((B, k), np.float64)
+    _check(load().orc_route(_p(logits), _p(ids), _p(w), B, E, int(k)))
+    return ids, w
 
 
 def truth_layer(x, ids, w, f_gate, f_up, f_down):

@@ -29,13 +29,16 @@
  * buffers" (a BF16 per-expert output buffer that is combined afterwards); it
  * exists only to check the direction of the accuracy claim.
  *
+ * orc_route, at the end, is the top-k router step in front of the layer (the
+ * pages give no router details; the reading is stated there).
+ *
  * Format facts used (OCP 8-bit floating point and OCP Microscaling v1.0
  * specifications, not on the pages): E4M3 has 1 sign, 4 exponent (bias 7) and
  * 3 mantissa bits, no infinities, NaN = S.1111.111; E8M0 is an unsigned
  * biased exponent, value 2^(v-127), with 0xFF = NaN.
  *
- * Error returns: 0 = ok, -1 = null pointer, -2 = bad shape, -3 = expert id
- * outside [0, E).
+ * Error returns: 0 = ok, -1 = null pointer, -2 = bad shape (or a logit that
+ * is not finite), -3 = expert id outside [0, E).
  */
 #include <math.h>
 #include <stdint.h>
@@ -396,6 +399,59 @@ int orc_conventional(const uint16_t *x, const int32_t *ids, const float *tw,
         free(xq);
         free(hq);
         free(acc);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Router step in front of the layer                                   */
+/* ------------------------------------------------------------------ */
+
+/* The pages route each token to a few of many experts ("The traditional MoE
+ * path": 8 of 128 in one layer) and give no router details.  The reading
+ * used here, the plainest top-k router: from one FP32 logit per expert,
+ * token b keeps the k largest logits, largest first, the lower expert id
+ * first among equal logits; its routing weights are the softmax of all E
+ * logits restricted to the k kept experts and renormalised to sum to one
+ * (FP64 throughout).  Logits must be finite (-2 otherwise); B = 0 is a valid
+ * empty batch. */
+int orc_route(const float *logits, int32_t *ids_out, double *w_out, int B, int E, int k)
+{
+    long b, i;
+    int j;
+    if (!logits || !ids_out || !w_out)
+        return -1;
+    if (B < 0 || E <= 0 || k <= 0 || k > E)
+        return -2;
+    for (i = 0; i < (long)B * E; ++i)
+        if (!isfinite(logits[i]))
+            return -2;
+    for (b = 0; b < B; ++b) {
+        const float *l = logits + b * E;
+        char *taken = calloc((size_t)E, 1);
+        double m = -INFINITY, z = 0.0, s = 0.0;
+        if (!taken)
+            return -1;
+        /* selection: k times, the best expert not yet taken */
+        for (j = 0; j < k; ++j) {
+            long best = -1;
+            for (i = 0; i < E; ++i)
+                if (!taken[i] && (best < 0 || (double)l[i] > (double)l[best]))
+                    best = i;   /* strict >: an equal logit later in the list loses */
+            taken[best] = 1;
+            ids_out[b * k + j] = (int32_t)best;
+        }
+        /* softmax over all E experts, then renormalised over the kept k */
+        for (i = 0; i < E; ++i)
+            if ((double)l[i] > m)
+                m = l[i];
+        for (i = 0; i < E; ++i)
+            z += exp((double)l[i] - m);
+        for (j = 0; j < k; ++j)
+            s += exp((double)l[ids_out[b * k + j]] - m) / z;
+        for (j = 0; j < k; ++j)
+            w_out[b * k + j] = exp((double)l[ids_out[b * k + j]] - m) / z / s;
+        free(taken);
     }
     return 0;
 }

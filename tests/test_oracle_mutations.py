@@ -2,8 +2,8 @@
 
 Each case copies the oracle's C source, plants one mistake in the copy (a
 dropped sign, a wrong exponent bias or index, swapped operands, a wrong
-rounding rule, a dropped router weight ...), builds it into a temporary
-library, and runs the pin tests against it.  At least one pin has to fail for
+rounding rule, a dropped router weight, a wrong tie rule in the router ...),
+builds it into a temporary library, and runs the pin tests against it.  At least one pin has to fail for
 every planted mistake; the unmodified oracle passes all of them (the other test
 modules).  The planted mistakes only ever live in a temporary copy.
 """
@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_formats as F
 from tests import test_oracle_layer as L
+from tests import test_oracle_router as RT
 
 MUTATIONS = [
     ("e4m3 sign dropped", "return s ? -mag : mag;", "return mag;"),
@@ -36,6 +37,11 @@ MUTATIONS = [
     ("bf16 via fp32 (double rounding)", "r = nearbyint(a / spacing) * spacing;",
      "r = nearbyint((double)(float)a / spacing) * spacing;"),
     ("bf16 significand width", "spacing = ldexp(1.0, ex - 1 - 7);", "spacing = ldexp(1.0, ex - 1 - 8);"),
+    ("router ties to the higher id", "(double)l[i] > (double)l[best]", "(double)l[i] >= (double)l[best]"),
+    ("router keeps the smallest logits", "(double)l[i] > (double)l[best]", "(double)l[i] < (double)l[best]"),
+    ("router weights not renormalised", "- m) / z / s;", "- m) / z;"),
+    ("router weight of the wrong slot", "w_out[b * k + j] = exp((double)l[ids_out[b * k + j]] - m)",
+     "w_out[b * k + j] = exp((double)l[ids_out[b * k]] - m)"),
 ]
 
 PINS = [
@@ -49,6 +55,8 @@ PINS = [
     ("dense k=1", lambda o: L.test_k1_is_dense_swiglu_ffn(o)),
     ("permutation", lambda o: L.test_permutation_invariance(o)),
     ("linearity", lambda o: L.test_router_weight_linearity_and_special_cases(o)),
+    ("router ranks", lambda o: RT.test_route_matches_rank_definition(o, 12, 5)),
+    ("router k=2", lambda o: RT.test_route_k2_is_logistic_of_the_gap(o)),
 ]
 
 
