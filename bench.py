@@ -14,8 +14,9 @@ activations, routing, the intermediate's write and read, and the output
 copy-kernel peak measured in the same process (the efficiency figure of the
 blog post's "Hardware efficiency" section), a B sweep, the dominant kernel's
 roofline position, the conventional expert-centric path timed on the same
-batches (the blog post's "Stage elimination" A/B), and the CPU oracle timed
-on the host as a baseline.
+batches (the blog post's "Stage elimination" A/B), the top-k router step in
+front of the layer (fused into gate/up and as its own kernel), and the CPU
+oracle timed on the host as a baseline.
 
 Weights: one layer is generated on the host (seed 0) and uploaded into
 `--copies` separate device buffers; step i uses copy i mod copies, so
@@ -209,15 +210,30 @@ def main():
         ws = None
         if path == "conventional":   # the expert-centric A/B path: seven launches through a workspace
             ws = torch.empty(mg.moe_decode_conventional_workspace(B, H_, I_, E_, k_), dtype=torch.uint8, device=dev)
+        lgs = None
+        if path in ("routed", "route_kernel"):
+            # the router step in the timed loop: logits in (the draw behind the uniform
+            # routing, so the same ids), ids and weights written on the device
+            assert kind == "uniform"
+            lgs = up(np.stack([mi.router_logits(seed, B, E_, it=r) for r in range(n_rout)]))
+            rid = torch.empty((B, k_), dtype=torch.int32, device=dev)
+            rw = torch.empty((B, k_), dtype=torch.float32, device=dev)
 
         def layer(i):
+            wg, sg, wu, su, wd, sd = wcopies[i % len(wcopies)]
+            r = i % n_rout
             if ws is not None:
-                wg, sg, wu, su, wd, sd = wcopies[i % len(wcopies)]
-                r = i % n_rout
                 mg.moe_decode_conventional(xs[r], idss[r], wss[r], wg, sg, wu, su, wd, sd, y, ws)
-                return
-            gate_up(i)
-            down(i)
+            elif path == "routed":   # router step fused into gate/up, then down
+                mg.moe_decode_gate_up_routed(xs[r], lgs[r], wg, sg, wu, su, h, rid, rw)
+                mg.moe_decode_down(h, rid, rw, wd, sd, y)
+            elif path == "route_kernel":   # router kernel, then the two layer kernels
+                mg.moe_decode_route(lgs[r], rid, rw)
+                mg.moe_decode_gate_up(xs[r], rid, wg, sg, wu, su, h)
+                mg.moe_decode_down(h, rid, rw, wd, sd, y)
+            else:
+                gate_up(i)
+                down(i)
 
         def timed(fn, n):
             for i in range(warmup * layers):
@@ -303,6 +319,20 @@ def main():
             log(f"conventional path B={b}: {rc['us_per_layer']:.2f} us/layer vs warp decode "
                 f"{rw['us_per_layer']:.2f} us ({rc['us_per_layer'] / rw['us_per_layer']:.2f}x)")
         extra["conventional_ab"] = ab
+
+        # the router step (top-8 of 128 logits, softmax over the kept 8) in front of the
+        # layer: fused into gate/up vs its own kernel, against the layer with ids given
+        ra = []
+        for b in (1, 8, 32):
+            rw = warp.get(b) or brief(run_steps(copies, S1, b, args.sweep_steps, 10, args.routings, kernels=False))
+            rf = run_steps(copies, S1, b, args.sweep_steps, 10, args.routings, kernels=False, path="routed")
+            rk = run_steps(copies, S1, b, args.sweep_steps, 10, args.routings, kernels=False, path="route_kernel")
+            ra.append({"B": b, "ids_given_us_per_layer": round(rw["us_per_layer"], 3),
+                       "router_fused_us_per_layer": round(rf["us_per_layer"], 3),
+                       "router_kernel_us_per_layer": round(rk["us_per_layer"], 3)})
+            log(f"router step B={b}: fused {rf['us_per_layer']:.2f} us/layer, own kernel "
+                f"{rk['us_per_layer']:.2f}, ids given {rw['us_per_layer']:.2f}")
+        extra["router_ab"] = ra
 
         # 48-layer decode step: 48 weight copies at distinct addresses, fresh routing per layer
         deep = [copies[i % len(copies)] if i < len(copies) else [t.clone() for t in first] for i in range(48)]

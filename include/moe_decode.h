@@ -149,6 +149,45 @@ int moe_decode_down_ex(const void *h, const int32_t *topk_ids, const float *topk
                        int B, int H, int I, int E, int k,
                        int variant, int rows_per_wave, void *stream);
 
+/* Router step in front of the layer.  The blog post ("The traditional MoE
+ * path") routes each token to a few of many experts (8 of 128 in one layer)
+ * and gives no router details; these calls implement the plain top-k router:
+ * from logits fp32 [B, E] (row-major, finite values), token b keeps its k
+ * largest logits, largest first and the lower expert id first among equal
+ * logits (-0 equals +0), so topk_ids[b, j] is its j-th selection; the routing
+ * weight topk_weights[b, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
+ * k selections (the softmax over all E renormalised over the kept k), in
+ * FP32 with the device's expf.  Ids are always in [0, E), even for logits
+ * that are not finite (their weights are then unspecified).
+ * Limits: E <= 1024, k <= 64 and k <= E, B*E*4 < 2^31.  Pointers 4-byte
+ * aligned; outputs disjoint from each other and from every input.
+ *
+ *   moe_decode_route: ids and weights only (one 64-lane wavefront per token).
+ *   moe_decode_gate_up_routed: gate/up with the router step in front --
+ *     reads logits instead of topk_ids, writes h_out as moe_decode_gate_up
+ *     would for the ids it selects, and also writes topk_ids_out and
+ *     topk_weights_out [B, k] for moe_decode_down.  For E <= 128 and
+ *     B*k <= 16 (and whenever the _ex form asks for the per-slot variant
+ *     with E <= 128) the selection is the per-slot kernel's prologue: each
+ *     workgroup selects its token's experts itself, with no extra launch.
+ *     Otherwise the router kernel runs first and the table's (or the asked)
+ *     gate/up variant reads the ids it wrote: two launches on `stream`.  The
+ *     _ex form takes variant and rows_per_wave as moe_decode_gate_up_ex
+ *     does. */
+int moe_decode_route(const float *logits, int32_t *topk_ids, float *topk_weights,
+                     int B, int E, int k, void *stream);
+int moe_decode_gate_up_routed(const void *x, const float *logits,
+                              const uint8_t *w_gate, const uint8_t *s_gate,
+                              const uint8_t *w_up, const uint8_t *s_up,
+                              void *h_out, int32_t *topk_ids_out, float *topk_weights_out,
+                              int B, int H, int I, int E, int k, void *stream);
+int moe_decode_gate_up_routed_ex(const void *x, const float *logits,
+                                 const uint8_t *w_gate, const uint8_t *s_gate,
+                                 const uint8_t *w_up, const uint8_t *s_up,
+                                 void *h_out, int32_t *topk_ids_out, float *topk_weights_out,
+                                 int B, int H, int I, int E, int k,
+                                 int variant, int rows_per_wave, void *stream);
+
 /* The launch the built-in table picks for a call (for reports): writes the
  * variant, rows_per_wave and the number of workgroups; returns 0 or a
  * negative code. */

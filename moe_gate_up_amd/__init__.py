@@ -33,7 +33,8 @@ MOE_DOWN_EXPERT_GROUPED = 2
 EXPORTS = (
     "moe_decode_gate_up", "moe_decode_down", "moe_decode_gate_up_ex", "moe_decode_down_ex",
     "moe_decode_gate_up_plan", "moe_decode_down_plan", "moe_decode_conventional_workspace",
-    "moe_decode_conventional", "moe_decode_copy_peak", "moe_decode_read_peak",
+    "moe_decode_conventional", "moe_decode_route", "moe_decode_gate_up_routed", "moe_decode_gate_up_routed_ex",
+    "moe_decode_copy_peak", "moe_decode_read_peak",
     "moe_decode_strerror",
 )
 
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
             L.moe_decode_down_plan.argtypes = [I] * 5 + [IP, IP, IP]
             L.moe_decode_conventional_workspace.argtypes = [I] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
             L.moe_decode_conventional.argtypes = [P] * 11 + [S] + [I] * 5 + [P]
+            L.moe_decode_route.argtypes = [P] * 3 + [I] * 3 + [P]
+            L.moe_decode_gate_up_routed.argtypes = [P] * 9 + [I] * 5 + [P]
+            L.moe_decode_gate_up_routed_ex.argtypes = [P] * 9 + [I] * 7 + [P]
             L.moe_decode_copy_peak.argtypes = [P, P, S, P]
             L.moe_decode_read_peak.argtypes = [P, S, P, P]
             L.moe_decode_strerror.argtypes = [I]
@@ -130,6 +134,46 @@ def moe_decode_gate_up(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B=None, H
     if rc:
         raise MoeDecodeError(rc, "moe_decode_gate_up")
     return h_out
+
+
+def moe_decode_route(logits, topk_ids, topk_weights, B=None, E=None, k=None, stream=None):
+    """Top-k router: topk_ids / topk_weights [B,k] from logits fp32 [B,E] (see include/moe_decode.h)."""
+    T = _types()
+    B = logits.shape[0] if B is None else B
+    E = logits.shape[-1] if E is None else E
+    k = topk_ids.shape[-1] if k is None else k
+    rc = lib().moe_decode_route(
+        _dev(logits, "logits", B * E, T["f32"]), _dev(topk_ids, "topk_ids", B * k, T["i32"]),
+        _dev(topk_weights, "topk_weights", B * k, T["f32"]), B, E, k, _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_route")
+    return topk_ids, topk_weights
+
+
+def moe_decode_gate_up_routed(x, logits, w_gate, s_gate, w_up, s_up, h_out, topk_ids_out, topk_weights_out,
+                              B=None, H=None, I=None, E=None, k=None, stream=None, rows_per_wave=None, variant=None):
+    """gate/up with the top-k router step fused in: h_out, topk_ids_out and topk_weights_out
+    from x and the router logits (see include/moe_decode.h)."""
+    T = _types()
+    B = x.shape[0] if B is None else B
+    H = x.shape[-1] if H is None else H
+    k = topk_ids_out.shape[-1] if k is None else k
+    E = w_gate.shape[0] if E is None else E
+    I = w_gate.shape[1] if I is None else I
+    args = [
+        _dev(x, "x", B * H, T["bf16"]), _dev(logits, "logits", B * E, T["f32"]),
+        _dev(w_gate, "w_gate", E * I * H, T["u8"]), _dev(s_gate, "s_gate", E * I * (H // 32), T["u8"]),
+        _dev(w_up, "w_up", E * I * H, T["u8"]), _dev(s_up, "s_up", E * I * (H // 32), T["u8"]),
+        _dev(h_out, "h_out", B * k * I, T["bf16"]), _dev(topk_ids_out, "topk_ids_out", B * k, T["i32"]),
+        _dev(topk_weights_out, "topk_weights_out", B * k, T["f32"]), B, H, I, E, k,
+    ]
+    if rows_per_wave is None and variant is None:
+        rc = lib().moe_decode_gate_up_routed(*args, _stream(stream))
+    else:
+        rc = lib().moe_decode_gate_up_routed_ex(*args, int(variant or 0), int(rows_per_wave or 0), _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_gate_up_routed")
+    return h_out, topk_ids_out, topk_weights_out
 
 
 def moe_decode_down(h, topk_ids, topk_weights, w_down, s_down, y_out, B=None, H=None, I=None, E=None, k=None,

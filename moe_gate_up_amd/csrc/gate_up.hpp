@@ -26,18 +26,28 @@
 // workgroups are remapped so that each XCD runs a contiguous range of tiles.
 // All tokens that share an expert then read that expert's rows at about the
 // same time on the same XCD, and the repeats hit that XCD's L2.
+//
+// ROUTE (E <= 128): the router step is the kernel's prologue.  The
+// workgroup reads its token's E logits instead of ids, selects the token's
+// top k itself (the same selection as the router kernel: once per workgroup
+// when its 4 wavefronts share the token, else once per wavefront) and takes
+// selection j for slot j; the first neuron tile also stores the ids and the
+// routing weights for the down kernel.  The x loads are issued before the
+// selection, so they are in flight while it runs.
 #pragma once
 
 #include "prims.hpp"
+#include "router.hpp"
 
 namespace moe {
 
-template <int NCH, int R, bool XL>
+template <int NCH, int R, bool XL, bool ROUTE>
 __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
     const uint8_t* __restrict__ wu, const uint8_t* __restrict__ su,
-    uint16_t* __restrict__ h, int B, int H, int I, int E, int k, int n_tiles) {
+    uint16_t* __restrict__ h, int B, int H, int I, int E, int k, int n_tiles,
+    const float* __restrict__ logits, int32_t* __restrict__ ids_out, float* __restrict__ tw_out) {
   const int lane = threadIdx.x & 63;
   // wave-uniform: keep the index math in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(xcd_contiguous_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6));
@@ -51,9 +61,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
   const int b = __builtin_amdgcn_readfirstlane(s / k);
   const int n0 = tile * R;
   const int nblk = H >> 5;
-  const int e_raw = __builtin_amdgcn_readfirstlane(ids[s]);
-  const bool bad = (unsigned)e_raw >= (unsigned)E;
-  const int e = bad ? 0 : e_raw;
+  int e_raw = 0;
+  if constexpr (!ROUTE) e_raw = __builtin_amdgcn_readfirstlane(ids[s]);
 
   // element offset of this lane's 16-element chunk in pass c, clamped to the
   // row; the scale bias zeroes the clamped duplicates
@@ -89,6 +98,43 @@ __global__ __launch_bounds__(256) void moe_gate_up_3d_batched_w64(
       xa[c][1] = bload16(xr, off[c] * 2u + 16u, xoff);
     }
   }
+
+  if constexpr (ROUTE) {
+    constexpr int NV = route_per_lane(kRouteFusedMaxExperts);
+    const int w_in = threadIdx.x >> 6;
+    // XL: the workgroup's 4 slots j0 .. j0+3 share the token; wavefront 0
+    // selects once and hands the experts over through LDS.  Else every
+    // wavefront selects for its own slot.
+    const int s0 = XL ? s - w_in : s, nsl = XL ? 4 : 1;
+    if (!XL || w_in == 0) {
+      const int j0 = s0 - b * k;
+      const RouteSel rs = wave_select<NV>(logits + (size_t)b * E, E, k, lane);
+      if constexpr (XL) {
+        extern __shared__ __attribute__((aligned(16))) uint8_t lds_x[];
+        int* sel = reinterpret_cast<int*>(lds_x + 2 * H);
+        for (int i = 0; i < 4; ++i) {
+          const int ei = route_expert(rs, j0 + i);
+          if (lane == 0) sel[i] = ei;
+        }
+      } else {
+        e_raw = route_expert(rs, j0);
+      }
+      if (tile == 0) {   // the first neuron tile also stores ids and weights of its slots
+        const float w = route_weight(rs, k, lane);
+        if (lane >= j0 && lane < j0 + nsl) {
+          ids_out[s0 + lane - j0] = rs.id;
+          tw_out[s0 + lane - j0] = w;
+        }
+      }
+    }
+    if constexpr (XL) {
+      extern __shared__ __attribute__((aligned(16))) uint8_t lds_x[];
+      __syncthreads();
+      e_raw = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(lds_x + 2 * H)[w_in]);
+    }
+  }
+  const bool bad = (unsigned)e_raw >= (unsigned)E;
+  const int e = bad ? 0 : e_raw;
 
   u32x4 gw[R][NCH], uw[R][NCH];
   uint32_t gsc[R][NCH], usc[R][NCH];

@@ -12,6 +12,7 @@
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
 #include "peak.hpp"
+#include "router.hpp"
 
 namespace {
 
@@ -60,33 +61,87 @@ int gate_up_default_rows(int B, int H, int I, int k) {
   return r;
 }
 
+// The router step in front of gate/up: logits in, ids and routing weights out.
+struct RouteIO {
+  const float* logits;   // [B, E]
+  int32_t* ids;          // [B, k]
+  float* tw;             // [B, k]
+  bool fuse;             // as the per-slot kernel's prologue (else the router kernel first)
+};
+
+// The router step is fused into the per-slot kernel while B*k <= 16: every
+// workgroup selects its token's experts again (a few hundred dependent
+// instructions, ~1.5 us), which beats a launch of its own (~2.9 us per layer)
+// only while there are few workgroups per CU (graph-timed, H = 2048, I = 768,
+// 128 experts, top-8: 1 token 13.9 vs 15.3 us per layer, 2 tokens 20.2 vs
+// 21.8, 4 tokens 32.5 vs 32.6, 8 tokens 54.1 vs 52.1).  The fused kernel
+// takes 2 rows per wavefront (fewer workgroups, fewer selections).
+constexpr long long kRouteFusedMaxSlots = 16;
+constexpr int kRouteFusedRows = 2;
+
+// Router kernel: one wavefront per token, 4 tokens per workgroup.
+template <int NV>
+void launch_route_t(hipStream_t st, const RouteIO& ro, int B, int E, int k) {
+  hipLaunchKernelGGL((moe::moe_route_w64<NV>), dim3((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock)),
+                     dim3(64 * kWavesPerBlock), 0, st, ro.logits, ro.ids, ro.tw, B, E, k);
+}
+void launch_route(hipStream_t st, const RouteIO& ro, int B, int E, int k) {
+  switch (moe::route_per_lane(E)) {
+    case 1: return launch_route_t<1>(st, ro, B, E, k);
+    case 2: return launch_route_t<2>(st, ro, B, E, k);
+    case 4: return launch_route_t<4>(st, ro, B, E, k);
+    case 8: return launch_route_t<8>(st, ro, B, E, k);
+    default: return launch_route_t<16>(st, ro, B, E, k);
+  }
+}
+
 // Every gate/up launcher returns its number of workgroups and launches only
-// when `go` is set (the plan query calls it with go = false).
+// when `go` is set (the plan query calls it with go = false).  With `ro` set
+// the router step runs too: as the per-slot kernel's prologue if ro->fuse,
+// else as the router kernel before it.
 //
 // Per-slot grid: one wavefront per (tile of R neurons, slot).  k % 4 == 0:
 // the 4 wavefronts of a workgroup serve one token and share x[b] through LDS.
+template <int NCH, int R, bool ROUTE>
+void launch_gate_up_k(dim3 grid, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
+                      const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
+                      int k, int tiles, const RouteIO* ro) {
+  const float* lg = ro ? ro->logits : nullptr;
+  int32_t* io = ro ? ro->ids : nullptr;
+  float* to = ro ? ro->tw : nullptr;
+  if (k % 4 == 0)   // dynamic LDS: x[b], and with the router step the 4 slots' experts
+    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, true, ROUTE>), grid, dim3(64 * kWavesPerBlock),
+                       (unsigned)(2 * H + (ROUTE ? 16 : 0)), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu, su,
+                       static_cast<uint16_t*>(h), B, H, I, E, k, tiles, lg, io, to);
+  else
+    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, false, ROUTE>), grid, dim3(64 * kWavesPerBlock), 0,
+                       st, static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I,
+                       E, k, tiles, lg, io, to);
+}
+
 template <int NCH, int R>
 long long launch_gate_up_t(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
                            const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
-                           int k) {
+                           int k, const RouteIO* ro) {
   static_assert(kWavesPerBlock == 4, "x sharing assumes 4 slots per workgroup");
   const int tiles = (I + R - 1) / R;
   const long long blocks = ((long long)tiles * B * k + kWavesPerBlock - 1) / kWavesPerBlock;
   if (!go || blocks * kWavesPerBlock >= (1LL << 31)) return blocks;
   const dim3 grid((unsigned)blocks);
-  if (k % 4 == 0)
-    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, true>), grid, dim3(64 * kWavesPerBlock),
-                       (unsigned)(2 * H), st, static_cast<const uint16_t*>(x), ids, wg, sg, wu, su,
-                       static_cast<uint16_t*>(h), B, H, I, E, k, tiles);
-  else
-    hipLaunchKernelGGL((moe::moe_gate_up_3d_batched_w64<NCH, R, false>), grid, dim3(64 * kWavesPerBlock), 0, st,
-                       static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
-                       tiles);
+  if (ro && ro->fuse) {
+    launch_gate_up_k<NCH, R, true>(grid, st, x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles, ro);
+  } else {
+    if (ro) {
+      launch_route(st, *ro, B, E, k);
+      ids = ro->ids;
+    }
+    launch_gate_up_k<NCH, R, false>(grid, st, x, ids, wg, sg, wu, su, h, B, H, I, E, k, tiles, nullptr);
+  }
   return blocks;
 }
 
 using GateUpLaunch = long long (*)(bool, hipStream_t, const void*, const int32_t*, const uint8_t*, const uint8_t*,
-                                   const uint8_t*, const uint8_t*, void*, int, int, int, int, int);
+                                   const uint8_t*, const uint8_t*, void*, int, int, int, int, int, const RouteIO*);
 
 template <int NCH, int R>
 GateUpLaunch gate_up_fn() {
@@ -136,14 +191,22 @@ bool grouped_allowed(int nch, int r, long long slots, int E) {
 #define MOE_GROUPED_BLOCKS 2048
 #endif
 constexpr long long kGroupedBlocks = MOE_GROUPED_BLOCKS;
+//
+// With the router step, the router kernel runs first and the grouped kernel
+// reads the ids it wrote: every grouped workgroup needs every token's ids, so
+// selecting them in each workgroup would repeat B selections per workgroup.
 template <int NCH, int R>
 long long launch_grouped_t(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
                            const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
-                           int k) {
+                           int k, const RouteIO* ro) {
   const long long slots = (long long)B * k;   // work units (<= slots) x groups of 4 tiles
   const long long items_max = slots * (long long)((I + 4 * R - 1) / (4 * R));
   const long long blocks = items_max < kGroupedBlocks ? items_max : kGroupedBlocks;
   if (!go) return blocks;
+  if (ro) {
+    launch_route(st, *ro, B, E, k);
+    ids = ro->ids;
+  }
   hipLaunchKernelGGL((moe::moe_gate_up_expert_grouped_w64<NCH, R>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
                      (unsigned)moe::grouped_lds_bytes(E, (int)slots, H), st, static_cast<const uint16_t*>(x), ids, wg,
                      sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k);
@@ -217,25 +280,69 @@ GateUpLaunch gate_up_launcher(int& variant, int nch, int& rows, int B, int H, in
   return nullptr;
 }
 
+// Router limits: E logits per token held 16 per lane, selection j in lane j,
+// and 32-bit byte offsets into the logits.
+int check_route_shape(int B, int E, int k) {
+  if (B < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_SHAPE;
+  if (E > moe::kRouteMaxExperts || k > moe::kRouteMaxK) return MOE_ERR_SHAPE;
+  if ((long long)B * E * 4 >= (1LL << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// The router's outputs must not overlap its logits or each other.
+int check_route_io(const RouteIO& ro, int B, int E, int k) {
+  if (!ro.logits || !ro.ids || !ro.tw) return MOE_ERR_NULL;
+  if (!aligned(ro.logits, 4) || !aligned(ro.ids, 4) || !aligned(ro.tw, 4)) return MOE_ERR_ALIGN;
+  const size_t lb = (size_t)B * E * 4, ob = (size_t)B * k * 4;
+  if (overlaps(ro.ids, ob, ro.logits, lb) || overlaps(ro.tw, ob, ro.logits, lb) || overlaps(ro.ids, ob, ro.tw, ob))
+    return MOE_ERR_ALIAS;
+  return MOE_OK;
+}
+
+// ro == nullptr: ids are an input.  Else ids is unused and the router step
+// writes ro->ids and ro->tw from ro->logits.
 int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uint8_t* sg, const uint8_t* wu,
-                 const uint8_t* su, void* h, int B, int H, int I, int E, int k, int variant, int rows, void* stream) {
+                 const uint8_t* su, void* h, int B, int H, int I, int E, int k, int variant, int rows, void* stream,
+                 const RouteIO* ro = nullptr) {
   int rc = check_shape(B, H, I, E, k);
+  if (!rc && ro) rc = check_route_shape(B, E, k);
   if (rc) return rc;
   if (B == 0) return MOE_OK;
-  if (!x || !ids || !wg || !sg || !wu || !su || !h) return MOE_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(h, 16) || !aligned(ids, 4))
+  if (!x || (!ro && !ids) || !wg || !sg || !wu || !su || !h) return MOE_ERR_NULL;
+  if (ro && (rc = check_route_io(*ro, B, E, k))) return rc;
+  if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(h, 16) || (!ro && !aligned(ids, 4)))
     return MOE_ERR_ALIGN;
   const size_t hb = (size_t)B * k * I * 2, wb = (size_t)E * I * H, sb = wb / 32;
-  if (overlaps(h, hb, x, (size_t)B * H * 2) || overlaps(h, hb, ids, (size_t)B * k * 4) || overlaps(h, hb, wg, wb) ||
-      overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
+  if (overlaps(h, hb, x, (size_t)B * H * 2) || (!ro && overlaps(h, hb, ids, (size_t)B * k * 4)) ||
+      overlaps(h, hb, wg, wb) || overlaps(h, hb, wu, wb) || overlaps(h, hb, sg, sb) || overlaps(h, hb, su, sb))
     return MOE_ERR_ALIAS;
+  if (ro) {   // every output against every input and the other outputs
+    const size_t ob = (size_t)B * k * 4, lb = (size_t)B * E * 4;
+    const void* outs[] = {ro->ids, ro->tw};
+    for (const void* o : outs)
+      if (overlaps(o, ob, x, (size_t)B * H * 2) || overlaps(o, ob, wg, wb) || overlaps(o, ob, wu, wb) ||
+          overlaps(o, ob, sg, sb) || overlaps(o, ob, su, sb) || overlaps(o, ob, h, hb))
+        return MOE_ERR_ALIAS;
+    if (overlaps(h, hb, ro->logits, lb)) return MOE_ERR_ALIAS;
+  }
   const int nch = passes(H);
+  RouteIO rt{};
+  if (ro) {   // fused: the table's choice for small batches, or the per-slot variant asked for
+    rt = *ro;
+    const bool small = (long long)B * k <= kRouteFusedMaxSlots;
+    if (variant == 0 && small && E <= moe::kRouteFusedMaxExperts) {
+      variant = MOE_GATE_UP_PER_SLOT;
+      if (rows == 0 && gate_up_allowed(nch, kRouteFusedRows)) rows = kRouteFusedRows;
+    }
+    rt.fuse = variant == MOE_GATE_UP_PER_SLOT && E <= moe::kRouteFusedMaxExperts;
+    ro = &rt;
+  }
   GateUpLaunch fn = gate_up_launcher(variant, nch, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
-  const long long blocks = fn(false, nullptr, x, ids, wg, sg, wu, su, h, B, H, I, E, k);
+  const long long blocks = fn(false, nullptr, x, ids, wg, sg, wu, su, h, B, H, I, E, k, ro);
   if (blocks * kWavesPerBlock >= (1LL << 31)) return MOE_ERR_SHAPE;
   (void)hipGetLastError();
-  fn(true, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k);
+  fn(true, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, ro);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
@@ -501,6 +608,35 @@ int moe_decode_gate_up_ex(const void* x, const int32_t* topk_ids, const uint8_t*
   return gate_up_impl(x, topk_ids, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, variant, rows_per_wave, stream);
 }
 
+int moe_decode_route(const float* logits, int32_t* topk_ids, float* topk_weights, int B, int E, int k,
+                     void* stream) {
+  int rc = check_route_shape(B, E, k);
+  if (rc) return rc;
+  if (B == 0) return MOE_OK;
+  const RouteIO ro{logits, topk_ids, topk_weights, false};
+  if ((rc = check_route_io(ro, B, E, k))) return rc;
+  (void)hipGetLastError();
+  launch_route(static_cast<hipStream_t>(stream), ro, B, E, k);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int moe_decode_gate_up_routed(const void* x, const float* logits, const uint8_t* w_gate, const uint8_t* s_gate,
+                              const uint8_t* w_up, const uint8_t* s_up, void* h_out, int32_t* topk_ids_out,
+                              float* topk_weights_out, int B, int H, int I, int E, int k, void* stream) {
+  const RouteIO ro{logits, topk_ids_out, topk_weights_out, false};
+  return gate_up_impl(x, nullptr, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, 0, 0, stream, &ro);
+}
+
+int moe_decode_gate_up_routed_ex(const void* x, const float* logits, const uint8_t* w_gate, const uint8_t* s_gate,
+                                 const uint8_t* w_up, const uint8_t* s_up, void* h_out, int32_t* topk_ids_out,
+                                 float* topk_weights_out, int B, int H, int I, int E, int k, int variant,
+                                 int rows_per_wave, void* stream) {
+  if (rows_per_wave < 0 || variant < 0) return MOE_ERR_ARG;
+  const RouteIO ro{logits, topk_ids_out, topk_weights_out, false};
+  return gate_up_impl(x, nullptr, w_gate, s_gate, w_up, s_up, h_out, B, H, I, E, k, variant, rows_per_wave, stream,
+                      &ro);
+}
+
 int moe_decode_down(const void* h, const int32_t* topk_ids, const float* topk_weights, const uint8_t* w_down,
                     const uint8_t* s_down, void* y_out, int B, int H, int I, int E, int k, void* stream) {
   return down_impl(h, topk_ids, topk_weights, w_down, s_down, y_out, B, H, I, E, k, 0, 0, stream);
@@ -538,7 +674,8 @@ int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int
   if (!fn) return MOE_ERR_ARG;
   *variant = v;
   *rows_per_wave = r;
-  *workgroups = (int)fn(false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, E, k);
+  *workgroups =
+      (int)fn(false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, E, k, nullptr);
   return MOE_OK;
 }
 

@@ -177,6 +177,45 @@ def test_plans():
         mg.moe_decode_gate_up_plan(1, 100, 768, 128, 8)
 
 
+def rt(lg=A, ids=A + 1 * S, tw=A + 2 * S, B=2, E=128, k=8):
+    L = mg.lib()
+    return L.moe_decode_route(*[ctypes.c_void_p(p) for p in (lg, ids, tw)], B, E, k, None)
+
+
+def gr(x=A, lg=A + 1 * S, wg=A + 2 * S, sg=A + 3 * S, wu=A + 4 * S, su=A + 5 * S, h=A + 6 * S, ids=A + 7 * S,
+       tw=A + 8 * S, B=2, H=2048, I=768, E=128, k=8, rows=None, variant=0):
+    L = mg.lib()
+    args = [ctypes.c_void_p(p) for p in (x, lg, wg, sg, wu, su, h, ids, tw)] + [B, H, I, E, k]
+    if rows is None:
+        return L.moe_decode_gate_up_routed(*args, None)
+    return L.moe_decode_gate_up_routed_ex(*args, variant, rows, None)
+
+
+def test_router_arguments():
+    for fn in (rt, gr):
+        assert fn(B=0) == mg.MOE_OK
+        assert fn(B=-1) == mg.MOE_ERR_SHAPE
+        assert fn(k=0) == mg.MOE_ERR_SHAPE
+        assert fn(E=4, k=5) == mg.MOE_ERR_SHAPE                 # k > E
+        assert fn(E=1056, k=8) == mg.MOE_ERR_SHAPE              # E beyond 16 logits per lane
+        assert fn(E=256, k=65) == mg.MOE_ERR_SHAPE              # k beyond one selection per lane
+        assert fn(lg=0) == mg.MOE_ERR_NULL
+        assert fn(ids=0) == mg.MOE_ERR_NULL
+        assert fn(tw=0) == mg.MOE_ERR_NULL
+        assert fn(lg=A + 2) == mg.MOE_ERR_ALIGN
+        assert fn(ids=A + 7 * S + 2 if fn is gr else A + S + 2) == mg.MOE_ERR_ALIGN
+        assert fn(tw=A + 2 * S + 16, ids=A + 2 * S) == mg.MOE_ERR_ALIAS     # the two outputs overlap
+        assert fn(ids=A + 256) == mg.MOE_ERR_ALIAS                          # ids over the logits
+    assert rt(B=1 << 20, E=1024) == mg.MOE_ERR_SHAPE            # logits beyond 2^31 bytes
+    assert gr(x=0) == mg.MOE_ERR_NULL
+    assert gr(h=A + 8 * S + 16) == mg.MOE_ERR_ALIAS             # h over the router weights
+    assert gr(h=A + 1 * S + 64) == mg.MOE_ERR_ALIAS             # h over the logits
+    assert gr(ids=A + 2 * S + 64) == mg.MOE_ERR_ALIAS           # ids over the gate weights
+    assert gr(H=2047) == mg.MOE_ERR_SHAPE
+    assert gr(rows=3) == mg.MOE_ERR_ARG
+    assert gr(rows=1, variant=3) == mg.MOE_ERR_ARG
+
+
 def test_peak_argument_errors():
     L = mg.lib()
     v = ctypes.c_void_p
