@@ -342,9 +342,14 @@ def main():
             r = run_steps(deep, S1, b, 10, 2, 96, seed=4000, layers=48, kernels=False)
             r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
             r["layers"] = 48
-            c4.append(brief(r))
+            # the same step with each layer's routing made on the device from its N(0,1) logits
+            rr = run_steps(deep, S1, b, 10, 2, 96, seed=4000, layers=48, kernels=False, path="routed")
+            r["us_per_step_with_router"] = rr["us_per_step"]
+            c4.append(brief(r, keys=("B", "us_per_layer", "us_per_step", "GBps", "frac_of_copy_peak",
+                                     "distinct_experts", "layers", "us_per_step_with_router")))
             log(f"48-layer step B={b}: {r['us_per_step']:.1f} us/step, {r['us_per_layer']:.2f} us/layer, "
-                f"{r['GBps']:.0f} GB/s ({r['frac_of_copy_peak']:.1%})")
+                f"{r['GBps']:.0f} GB/s ({r['frac_of_copy_peak']:.1%}); with the router step "
+                f"{rr['us_per_step']:.1f} us/step")
         extra["decode_step_48_layers"] = c4
         del deep
         torch.cuda.empty_cache()
