@@ -15,8 +15,9 @@
 // each taking work items blockIdx.x, blockIdx.x + gridDim.x, ...  Every
 // workgroup first indexes the B*k <= 1024 slots by expert in LDS
 // (slot_index.hpp), which yields the routed experts and each one's slots, cut
-// into work units of at most 4M slots (four fillings of the LDS staging area
-// of M x rows), so that an expert shared by many tokens is spread over
+// into work units of at most min(4M, 16) slots (four fillings of the 32 KB
+// LDS staging area of M x rows), so that an expert shared by many tokens is
+// spread over
 // several workgroups while an expert with a handful of slots is one unit (its
 // rows read once).  Unrouted experts produce no work.  A work item is a work
 // unit times a group of 4R neurons:
@@ -40,8 +41,9 @@ namespace moe {
 
 constexpr int kGroupedMaxSlots = kSortMaxSlots;       // B*k limit of the expert-grouped variant
 constexpr int kGroupedMaxExperts = kSortMaxExperts;   // E limit
-constexpr int kGroupedXBytes = 16384;                 // LDS for staged activations
-constexpr int kGroupedUnitChunks = 4;                 // staging rounds per work unit
+constexpr int kGroupedXBytes = 32768;                 // LDS for staged activations
+constexpr int kGroupedUnitChunks = 4;                 // staging rounds per work unit, up to
+constexpr int kGroupedUnitMaxSlots = 16;              // slots per work unit
 
 // bytes of one staged x row (1 KB-padded) and rows per chunk (at most 8)
 constexpr int kGroupedMaxChunk = 8;
@@ -51,8 +53,12 @@ __host__ __device__ constexpr int grouped_chunk(int H) {
              ? 1
              : (kGroupedXBytes / grouped_xrow(H) > kGroupedMaxChunk ? kGroupedMaxChunk : kGroupedXBytes / grouped_xrow(H));
 }
-// slots per work unit: four fillings of the staging area
-__host__ __device__ constexpr int grouped_unit_slots(int H) { return kGroupedUnitChunks * grouped_chunk(H); }
+// slots per work unit: four fillings of the staging area, at most 16 (a hot
+// expert's slots are spread over several workgroups)
+__host__ __device__ constexpr int grouped_unit_slots(int H) {
+  return kGroupedUnitChunks * grouped_chunk(H) < kGroupedUnitMaxSlots ? kGroupedUnitChunks * grouped_chunk(H)
+                                                                      : kGroupedUnitMaxSlots;
+}
 // LDS layout: slot index | staged x [M rows]
 __host__ __device__ constexpr int grouped_lds_bytes(int E, int S, int H) {
   return slot_index_lds_bytes(E, S) + grouped_chunk(H) * grouped_xrow(H);
@@ -99,7 +105,8 @@ void moe_gate_up_expert_grouped_w64(
   const int pieces = XS >> 10;
   // x rows per chunk.  MCAP bounds it for this NCH (H > 1024 (NCH - 1), so a
   // staged row is more than 2 KB (NCH - 1)) and sizes the token registers.
-  constexpr int MCAP = NCH == 1 ? kGroupedMaxChunk : (8 / (NCH - 1) > 0 ? 8 / (NCH - 1) : 1);
+  constexpr int MC = kGroupedXBytes / 2048 / (NCH > 1 ? NCH - 1 : 1);
+  constexpr int MCAP = NCH == 1 || MC > kGroupedMaxChunk ? kGroupedMaxChunk : (MC > 0 ? MC : 1);
   const int M = min(grouped_chunk(H), MCAP);
 
   // ---- work items: (work unit = up to M slots of one routed expert, group of 4 tiles g)
