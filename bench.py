@@ -105,7 +105,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(the layer would shard I across GPUs with one all-reduce of y; not built).", file=sys.stderr)
         sys.exit(2)
 
