@@ -115,14 +115,14 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     the blog post's organisation ("How the two kernels work").  Best while
  *     few tokens share an expert.
  *   MOE_DOWN_EXPERT_GROUPED: one workgroup per 8 output dimensions (4 for
- *     I > 1024) for every token; its wavefronts split the routed experts
+ *     I > 1024) for every token; its wavefronts share out the routed experts
  *     (sorted on the device, in LDS), read each routed expert's rows once,
- *     and keep every token's FP32 sums in registers until the workgroup adds
- *     them and writes y once.  No per-expert output buffer, no combine.  Same
- *     outputs; requires
+ *     and keep each slot's FP32 contribution in LDS until the workgroup adds
+ *     every token's k contributions in slot order and writes y once.  No
+ *     per-expert output buffer, no combine.  Same outputs; requires
  *     B <= 64, B*k <= 1024, E <= 1024 and I <= 2048.
- * The plain call takes the grouped variant once B*k >= 2E (B*k >= E when
- * I > 1024) and the limits allow it, else the per-token one. */
+ * The plain call takes the grouped variant once B*k >= E (an average of one
+ * or more slots per expert) and the limits allow it, else the per-token one. */
 #define MOE_DOWN_PER_TOKEN 1
 #define MOE_DOWN_EXPERT_GROUPED 2
 

@@ -14,22 +14,21 @@
 //  1. index the B*k slots by expert in LDS (slot_index.hpp);
 //  2. the slots of each routed expert are cut into work units of at most 8
 //     (so that an expert shared by many tokens is spread over wavefronts);
-//     wavefront w takes the units w, w + NW, ...  For each it loads
+//     wavefront w starts with unit w and then takes the next unhanded unit
+//     from an LDS counter whenever it comes free.  For each unit it loads
 //     the expert's RO rows -- contiguous in memory, read as RO row passes
 //     where lane l takes the 16 bytes at 16 l (+1024 per pass) -- and their
 //     RO x I/32 E8M0 scales with one dword load per lane (moved to the
 //     lanes that use them with ds_bpermute), then for every slot routed to
 //     the expert loads that slot's h row, forms the RO dot products (E4M3 ->
 //     bf16, v_dot2c_f32_bf16, v_ldexp_f32 per 16-element partial), sums them
-//     across the wave with one reduce-scatter and adds router weight x sum to
-//     RO FP32 accumulators of the slot's token, which live in lane b of the
-//     wavefront (B <= 64);
-//  3. the NW wavefronts' accumulators meet in LDS and thread (b, r) adds them
-//     in wavefront order and writes y[b, o0 + r] once.
-// Within a wavefront each token's sum runs over its units in order (experts
-// ascending, slots in slot order); across wavefronts in wavefront order: the
-// result does not depend on timing.  Outputs of a token with an
-// invalid id, or touching a row with a NaN scale code, are NaN.
+//     across the wave with one reduce-scatter and stores router weight x sum
+//     for each of the RO outputs as the slot's contribution in LDS;
+//  3. thread (b, r) adds token b's k slot contributions in slot order and
+//     writes y[b, o0 + r] once.
+// The sum of every output runs in slot order whichever wavefront computed a
+// slot's contribution: the result does not depend on timing.  Outputs of a
+// token with an invalid id, or touching a row with a NaN scale code, are NaN.
 #pragma once
 
 #include "slot_index.hpp"
@@ -45,9 +44,10 @@ constexpr int kDownGroupedUnitSlots = 8;   // slots per work unit: a hot expert 
 // two passes: 4 output dimensions per workgroup of 8 wavefronts.
 __host__ __device__ constexpr int down_grouped_rows(int np) { return np <= 1 ? 8 : 4; }
 __host__ __device__ constexpr int down_grouped_waves(int np) { return np <= 1 ? 16 : 8; }
-// LDS layout: slot index | per-wavefront accumulators [NW][RO][64] floats | NaN masks [NW][64]
+// LDS layout: slot index | per-slot contributions [S][RO] floats | per-slot
+// NaN masks [S] | next-unit counter
 __host__ __device__ constexpr int down_grouped_lds_bytes(int np, int E, int S) {
-  return slot_index_lds_bytes(E, S) + down_grouped_waves(np) * 64 * (down_grouped_rows(np) + 1) * 4;
+  return slot_index_lds_bytes(E, S) + S * (down_grouped_rows(np) + 1) * 4 + 16;
 }
 
 template <int NP>
@@ -65,9 +65,14 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int o0 = blockIdx.x * RO;
+  float* contrib = reinterpret_cast<float*>(lds + slot_index_lds_bytes(E, slots));   // [S][RO]
+  uint32_t* nanmask = reinterpret_cast<uint32_t*>(contrib + slots * RO);            // [S]
+  int* next_unit = reinterpret_cast<int*>(nanmask + slots);
+  // zero (a slot with an invalid id belongs to no unit) -- ordered before the
+  // unit loop by the index build's barriers
+  for (int i = tid; i < slots * (RO + 1); i += NT) contrib[i] = 0.0f;
+  if (tid == 0) *next_unit = NW;   // units 0 .. NW-1 go to wavefronts 0 .. NW-1
   const SlotIndex si = build_slot_index<NT>(lds, ids, slots, E, k, kDownGroupedUnitSlots);
-  float* accs = reinterpret_cast<float*>(lds + slot_index_lds_bytes(E, slots));   // [NW][RO][64]
-  uint32_t* nans = reinterpret_cast<uint32_t*>(accs + NW * RO * 64);             // [NW][64]
 
   const int nblk = I >> 5;
   uint32_t off[NP];
@@ -82,10 +87,9 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   const rsrc_t wr = make_rsrc(wd, wbytes), sr = make_rsrc(sd, wbytes / 32);
   const rsrc_t hr = make_rsrc(h, (uint64_t)slots * I * 2), twr = make_rsrc(tw, (uint64_t)slots * 4);
 
-  float acc[RO];   // lane b: token b's partial sums of y[b, o0 + r]
+  int r_lane = -1;   // the output row whose total this lane holds after the reduce-scatter
 #pragma unroll
-  for (int r = 0; r < RO; ++r) acc[r] = 0.0f;
-  uint32_t nanacc = 0;   // lane b: bit r set once a NaN scale touched y[b, o0 + r]
+  for (int r = 0; r < RO; ++r) r_lane = (lane == scatter_lane<RO>(r)) ? r : r_lane;
 
   // the expert's RO rows and their scales (row0 * nblk is a multiple of 4: H
   // and o0 are multiples of 4); dword t of lane l holds scale bytes 256 t + 4 l ..
@@ -169,15 +173,13 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
             for (int c = 0; c < NP; ++c) p[r] += apply_e8m0(chunk_dot(wv[r][c], hv[m][c], 0.0f), sc[r][c], bias[c]);
           }
           const float tot = wave_reduce_scatter<RO>(p, lane);
-          const int b = __builtin_amdgcn_readfirstlane((int)(si.sorted[first + m0 + m] >> 16));
+          const int sl = __builtin_amdgcn_readfirstlane((int)(si.sorted[first + m0 + m] & 0xFFFFu));
           const float wsm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ws[m])));
-          const float fw = lane == b ? wsm : 0.0f;   // only token b's lane accumulates
-#pragma unroll
-          for (int r = 0; r < RO; ++r) {
-            const float sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tot), scatter_lane<RO>(r)));
-            acc[r] = fmaf(fw, sum, acc[r]);
-          }
-          nanacc |= lane == b ? nan_rows : 0u;
+          // the slot's weighted contribution to its token's RO outputs, kept
+          // per slot: the final sum runs over slots in a fixed order, whichever
+          // wavefront computed them
+          if (r_lane >= 0) contrib[sl * RO + r_lane] = wsm * tot;
+          if (lane == 0) nanmask[sl] = nan_rows;
         }
       }
       // An unconditional use of every load of the round, after all of its
@@ -193,29 +195,35 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
     }
     };
 
-  // The first unit is processed outside the loop and its rows are loaded
+  // Units are handed out as wavefronts come free (an LDS counter): units
+  // differ in slot count and in memory latency, and a fixed round-robin left
+  // a workgroup's slowest wavefront finishing long after its fastest.  The
+  // first unit is processed outside the loop and its rows are loaded
   // unconditionally (a wavefront without a unit reads rows it will not use),
   // so no row register is merged across a branch or carried around the loop:
   // either made the compiler wait for the loads right away.
   load_rows(si.n_units > 0 ? si.unit_expert(min(w, si.n_units - 1)) : 0);
-  if (w < si.n_units) process(w);
-  for (int un = w + NW; un < si.n_units; un += NW) {
-    load_rows(si.unit_expert(un));
-    process(un);
+  if (w < si.n_units) {
+    process(w);
+    for (;;) {
+      int un = 0;
+      if (lane == 0) un = atomicAdd(next_unit, 1);
+      un = __builtin_amdgcn_readfirstlane(un);
+      if (un >= si.n_units) break;
+      load_rows(si.unit_expert(un));
+      process(un);
+    }
   }
 
-  // ---- the wavefronts' partial sums meet in LDS; thread (b, r) adds them in wavefront order
-#pragma unroll
-  for (int r = 0; r < RO; ++r) accs[(w * RO + r) * 64 + lane] = acc[r];
-  nans[w * 64 + lane] = nanacc;
+  // ---- thread (b, r) adds its token's k slot contributions in slot order
   __syncthreads();
   for (int t = tid; t < B * RO; t += NT) {
     const int b = t / RO, r = t - b * RO;
     float sum = 0.0f;
     uint32_t nn = 0;
-    for (int v = 0; v < NW; ++v) {
-      sum += accs[(v * RO + r) * 64 + b];
-      nn |= nans[v * 64 + b];
+    for (int j = 0; j < k; ++j) {
+      sum += contrib[(b * k + j) * RO + r];
+      nn |= nanmask[b * k + j];
     }
     bool nan_out = (nn >> r) & 1u;
     if (si.n_bad > 0) {   // a token with an invalid id is NaN everywhere

@@ -442,15 +442,13 @@ DownLaunch pick_down_grouped(int np) {
 
 // Variant table (graph-timed sweeps on MI355X, 128 experts, top-8, uniform
 // routing): the per-token kernel while few tokens share an expert, the
-// expert-grouped one from two slots per expert on (H = 2048, I = 768: 32
-// tokens 43.5 vs 46.4 us, 16 tokens 29.6 vs 28.5), or from one slot per
-// expert on with two passes over I (H = 4096, I = 1536: 16 tokens 103 vs
-// 115 us, 64 tokens 245 vs 364).
+// expert-grouped one from one slot per expert on (H = 2048, I = 768: 16
+// tokens 27.1 vs 28.6 us, 24 tokens 32.7 vs 38.0, 8 tokens 19.1 vs 18.2;
+// H = 4096, I = 1536: 16 tokens 105 vs 116 us, 8 tokens 65.6 vs 65.0).
 int down_default_variant(int B, int H, int I, int E, int k) {
   (void)H;
   const long long slots = (long long)B * k;
-  const long long need = passes(I) >= 2 ? (long long)E : 2LL * E;
-  if (slots >= need && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
+  if (slots >= E && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
   return MOE_DOWN_PER_TOKEN;
 }
 

@@ -171,7 +171,7 @@ def test_plans():
             assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * B // 4)
         else:                              # one workgroup per 8 output dimensions
             assert v == mg.MOE_DOWN_EXPERT_GROUPED and r == 8 and g == 2048 // 8
-        assert (v == mg.MOE_DOWN_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
+        assert (v == mg.MOE_DOWN_EXPERT_GROUPED) == (B * 8 >= 128)
     assert mg.moe_decode_down_plan(100, 2048, 768, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN   # B > 64
     with pytest.raises(mg.MoeDecodeError):
         mg.moe_decode_gate_up_plan(1, 100, 768, 128, 8)
