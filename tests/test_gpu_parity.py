@@ -5,7 +5,8 @@ every token row's cosine >= 0.999995; the oracle rounds FP64 to bf16 once, the
 GPU accumulates in FP32, so a few elements may differ by one bf16 step.
 Covered: every E4M3 code and E8M0 edge scale through the real kernel, small
 shapes spanning several tiles with ragged tails and every rows-per-wave
-variant, the five synthetic workloads at full size (the 48- and 8-layer
+variant, 24 seeded random shapes (ragged H, I, E, k, B; both kernel families;
+uniform or skewed routing), the five synthetic workloads at full size (the 48- and 8-layer
 workloads on a subset of their layers, the B=64 wide shape on sampled
 tokens), empty batches, out-of-range expert ids, full coverage of the outputs
 (sentinels and guard words), determinism and non-default streams.
@@ -143,6 +144,46 @@ def test_small_shapes_all_variants(dev, small_layers, shape, rows, variant):
     h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn, variant=variant)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
     check(h, y, h_ref, y_ref, B, k, f"{shape} rows={rows} variant={variant}")
+
+
+def _random_case(i):
+    """Seeded random shape within the kernels' limits, its routing and launch choices."""
+    g = np.random.default_rng(9000 + i)
+    k = int(g.integers(1, 9))
+    E = int(g.integers(k, 41))
+    B = int(g.integers(1, 41))
+    H = 32 * int(g.integers(1, 97))      # up to 3072
+    I = 32 * int(g.integers(1, 49))      # up to 1536
+    while k * I > 16384:
+        I -= 32
+    variant = FAMILIES[int(g.integers(0, 2))]
+    skew = bool(g.integers(0, 2))        # Zipf-like popularity: tokens share experts
+    return B, H, I, E, k, variant, skew, int(g.integers(0, 4))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(dev, i):
+    """Random shapes, ragged everywhere, both kernel families, random rows per wave
+    (the table's choice when the draw is beyond a kernel's limits), uniform or
+    skewed routing; against the oracle."""
+    B, H, I, E, k, variant, skew, rsel = _random_case(i)
+    D = DevLayer(mi.make_layer(9100 + i, H, I, E), dev)
+    x = mi.make_x(9200 + i, B, H)
+    ids, w = (mi.route_zipf if skew else mi.route_uniform)(9300 + i, B, E, k)
+    n_gu, n_dn = -(-H // 1024), -(-(k * I) // 1024)
+    rows = (1, 2, 4, 8)[rsel]
+    if variant == PER_SLOT:
+        rows_gu = rows if rows * n_gu <= 16 else None
+        rows_dn = rows if n_dn * (5 * rows + 8) <= 224 else None
+    else:
+        rows_gu = rows if rows * n_gu <= 8 else None
+        rows_dn = None
+        if -(-I // 1024) > 2 or B > 64:   # beyond the grouped down kernel's limits
+            variant = (mg.MOE_GATE_UP_EXPERT_GROUPED, mg.MOE_DOWN_PER_TOKEN)
+    h, y = run_gpu(D, x, ids, w, dev, rows_gu, rows_dn, variant=variant)
+    h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
+    check(h, y, h_ref, y_ref, B, k, f"random {i}: B={B} H={H} I={I} E={E} k={k} variant={variant} "
+                                    f"rows={rows_gu},{rows_dn} skew={skew}")
 
 
 @pytest.mark.parametrize("variant", FAMILIES, ids=["per_slot", "grouped"])
