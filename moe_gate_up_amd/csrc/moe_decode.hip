@@ -185,8 +185,8 @@ bool grouped_allowed(int nch, int r, long long slots, int E) {
 
 // Persistent grid of at most 2048 workgroups (8 per CU of MI355X's 256;
 // 1024 to 2560 measured within 4 %) and never more than the largest possible
-// number of work items; dynamic LDS: per-expert counters, sorted slots and
-// staged activations.
+// number of work item pairs; dynamic LDS: per-expert counters, sorted slots
+// and staged activations.
 #ifndef MOE_GROUPED_BLOCKS
 #define MOE_GROUPED_BLOCKS 2048
 #endif
@@ -201,7 +201,8 @@ long long launch_grouped_t(bool go, hipStream_t st, const void* x, const int32_t
                            int k, const RouteIO* ro) {
   const long long slots = (long long)B * k;   // work units (<= slots) x groups of 4 tiles
   const long long items_max = slots * (long long)((I + 4 * R - 1) / (4 * R));
-  const long long blocks = items_max < kGroupedBlocks ? items_max : kGroupedBlocks;
+  const long long pairs = (items_max + 1) / 2;   // a workgroup takes its items in pairs
+  const long long blocks = pairs < kGroupedBlocks ? pairs : kGroupedBlocks;
   if (!go) return blocks;
   if (ro) {
     launch_route(st, *ro, B, E, k);

@@ -160,7 +160,7 @@ def test_plans():
             assert g == -(-((768 + r - 1) // r) * B * 8 // 4)
         else:                              # persistent: <= 2048 workgroups, <= the possible work items
             assert v == mg.MOE_GATE_UP_EXPERT_GROUPED
-            assert g == min(2048, B * 8 * -(-768 // (4 * r)))
+            assert g == min(2048, -(-(B * 8 * -(-768 // (4 * r))) // 2))   # items taken in pairs
         # grouped once the batch averages two or more slots per expert
         assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
