@@ -229,8 +229,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// SiLU(g) = g / (1 + e^-g).  A gate that overflowed FP32 to -inf gets the
+// limit, -0 (the quotient would be -inf / inf = NaN); +inf stays +inf.
 __device__ __forceinline__ float silu(float g) {
-  return g / (1.0f + __expf(-g));
+  return g == -__builtin_huge_valf() ? -0.0f : g / (1.0f + __expf(-g));
 }
 
 // MI355X dispatches workgroup g to XCD (g mod 8); each XCD has its own L2.

@@ -50,7 +50,7 @@ struct SlotIndex {
 
 template <int NT>
 __device__ SlotIndex build_slot_index(uint8_t* lds, const int32_t* __restrict__ ids, int slots, int E, int k, int ch) {
-  constexpr int J = kSortMaxSlots / NT;
+  constexpr int J = (kSortMaxSlots + NT - 1) / NT;   // slots per thread, enough for kSortMaxSlots
   SlotIndex o;
   o.ch = ch;
   o.end_ = reinterpret_cast<int*>(lds);

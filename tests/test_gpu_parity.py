@@ -103,6 +103,36 @@ def test_every_e4m3_code_through_down_kernel(dev, scale, dvariant):
     assert np.array_equal(gv[ok], rv[ok]), np.nonzero(gv != rv)
 
 
+@pytest.mark.parametrize("scale", [127, 120, 134, 1, 0, 253, 255])
+@pytest.mark.parametrize("gvariant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED])
+def test_every_e4m3_code_through_gate_up_kernel(dev, scale, gvariant):
+    """Neuron n's gate row holds E4M3 code n in element 0 with E8M0 scale `scale`, its up
+    row 1.0 * 2^0, and x = e_0: gate = dec(n) * 2^(scale-127) and up = 1 exactly, so
+    h[n] = bf16(SiLU(gate)).  NaN codes (0x7F, 0xFF) and the NaN scale 255 give NaN, an
+    infinite gate infinity (or -0); everything else meets the layer's bar."""
+    E, H, I, k, B = 1, 32, 256, 1, 1
+    wg = np.zeros((E, I, H), np.uint8)
+    wg[0, :, 0] = np.arange(256, dtype=np.uint8)
+    sg = np.full((E, I, H // 32), scale, np.uint8)
+    wu = np.zeros((E, I, H), np.uint8)
+    wu[0, :, 0] = 0x38                   # E4M3 1.0
+    su = np.full((E, I, H // 32), 127, np.uint8)
+    x = np.zeros((B, H), np.uint16)
+    x[0, 0] = 0x3F80                      # 1.0
+    ids = np.zeros((B, k), np.int32)
+    h = torch.empty((B, k, I), dtype=torch.int16, device=dev)
+    mg.moe_decode_gate_up(_t(x, dev), _t(ids, dev), _t(wg, dev), _t(sg, dev), _t(wu, dev), _t(su, dev), h,
+                          variant=gvariant)
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(h.cpu().numpy().view(np.uint16).ravel())
+    ref = oracle.bf16_to_f64(oracle.gate_up(x, ids, wg, sg, wu, su).ravel())
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), np.nonzero(np.isnan(got) != np.isnan(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[~fin & ~np.isnan(ref)], ref[~fin & ~np.isnan(ref)])   # infinities exactly
+    err = np.abs(got[fin] - ref[fin])
+    assert np.all(err <= 2e-3 + 1e-2 * np.abs(ref[fin])), (scale, np.max(err))
+
+
 # --------------------------------------------------------------- small shapes
 SMALL = [
     # B, H, I, E, k
