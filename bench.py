@@ -174,7 +174,7 @@ def main():
     S = mi.SHAPES["S1"]
     H, I, E, k = S["H"], S["I"], S["E"], S["k"]
     t0 = time.time()
-    L = mi.make_layer(mi.layer_seed(2), H, I, E)
+    L = mi.make_layer(mi.layer_seed("batch_sweep"), H, I, E)
     log(f"generated layer in {time.time() - t0:.1f}s ({L.nbytes / 1e6:.1f} MB)")
 
     def up(a):
@@ -225,7 +225,7 @@ def main():
         for the launches and not the Python launch overhead, which at small B
         exceeds the kernels' own duration.  Warm-up passes run eagerly first."""
         H_, I_, E_, k_ = shape
-        seed = mi.routing_seed(2, B) if seed is None else seed
+        seed = mi.routing_seed("batch_sweep", B) if seed is None else seed
         xs, idss, wss, info = make_batch(shape, B, n_rout, kind, seed)
         h = torch.empty((B, k_, I_), dtype=torch.int16, device=dev)
         y = torch.empty((B, H_), dtype=torch.int16, device=dev)
@@ -331,7 +331,7 @@ def main():
         c3 = []
         for kind in ("zipf", "adversarial", "contiguous"):
             r = run_steps(copies, S1, 32, args.sweep_steps, 10, args.routings, kind=kind,
-                          seed=mi.routing_seed(3, 32, kind))
+                          seed=mi.routing_seed("routing_stress", 32, kind))
             r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
             r["routing"] = kind
             c3.append(brief(r))
@@ -390,7 +390,7 @@ def main():
         # wider expert shape: H=4096, I=1536, 8 layers
         S2d = mi.SHAPES["S2"]
         t0 = time.time()
-        L2 = mi.make_layer(mi.layer_seed(5, 0), S2d["H"], S2d["I"], S2d["E"])
+        L2 = mi.make_layer(mi.layer_seed("wide_layers", 0), S2d["H"], S2d["I"], S2d["E"])
         wide = [[up(a) for a in (L2.w_gate, L2.s_gate, L2.w_up, L2.s_up, L2.w_down, L2.s_down)]]
         del L2
         wide += [[t.clone() for t in wide[0]] for _ in range(7)]
@@ -399,7 +399,7 @@ def main():
         c5 = []
         S2 = (S2d["H"], S2d["I"], S2d["E"], S2d["k"])
         for b in (1, 16, 32, 64):
-            r = run_steps(wide, S2, b, args.sweep_steps // 2, 5, 32, seed=mi.routing_seed(5, b))
+            r = run_steps(wide, S2, b, args.sweep_steps // 2, 5, 32, seed=mi.routing_seed("wide_layers", b))
             r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
             c5.append(brief(r))
             log(f"H=4096/I=1536 B={b}: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s "
@@ -415,7 +415,7 @@ def main():
         cores = oracle.set_threads(0)
         rng_steps, spent, byt, n = 0, 0.0, 0, 0
         while spent < args.cpu_seconds and n < 64:
-            seed = mi.routing_seed(2, B)
+            seed = mi.routing_seed("batch_sweep", B)
             x = mi.make_x(seed, B, H, it=n)
             ids, w = mi.route_uniform(seed, B, E, k, it=n)
             c0 = time.perf_counter()

@@ -24,5 +24,5 @@ from .gen import (  # noqa: F401
     layer_seed,
     routing_seed,
     SHAPES,
-    CONFIGS,
+    WORKLOADS,
 )

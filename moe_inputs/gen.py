@@ -261,38 +261,41 @@ def make_routing(kind: str, seed: int, B: int, E: int, k: int, it: int = 0):
 # --------------------------------------------------------------------------
 # The five synthetic workloads
 # --------------------------------------------------------------------------
-CONFIGS = {
-    1: dict(name="single layer, B=1", shape="S1", batches=(1,), routings=("uniform",), layers=1),
-    2: dict(name="single layer, batch sweep", shape="S1", batches=(1, 2, 4, 8, 16, 32), routings=("uniform",), layers=1),
-    3: dict(name="B=32 routing stress", shape="S1", batches=(32,), routings=("zipf", "adversarial", "contiguous"), layers=1),
-    4: dict(name="48-layer decode step", shape="S1", batches=(1, 8, 32), routings=("uniform",), layers=48),
-    5: dict(name="larger expert shape, 8 layers", shape="S2", batches=(1, 16, 32, 64), routings=("uniform",), layers=8),
+WORKLOADS = {
+    "single_b1": dict(name="single layer, B=1", shape="S1", batches=(1,), routings=("uniform",), layers=1),
+    "batch_sweep": dict(name="single layer, batch sweep", shape="S1", batches=(1, 2, 4, 8, 16, 32), routings=("uniform",),
+                        layers=1),
+    "routing_stress": dict(name="B=32 routing stress", shape="S1", batches=(32,),
+                           routings=("zipf", "adversarial", "contiguous"), layers=1),
+    "decode_step": dict(name="48-layer decode step", shape="S1", batches=(1, 8, 32), routings=("uniform",), layers=48),
+    "wide_layers": dict(name="larger expert shape, 8 layers", shape="S2", batches=(1, 16, 32, 64), routings=("uniform",),
+                        layers=8),
 }
 
 _ROUTE_BASE = {"zipf": 3000, "adversarial": 3100, "contiguous": 3200}
 
 
-def layer_seed(config: int, layer: int = 0) -> int:
-    """Weight seed of layer `layer` of a config (configs 1-3 share layer seed 0)."""
-    if config in (1, 2, 3):
+def layer_seed(workload: str, layer: int = 0) -> int:
+    """Weight seed of layer `layer` of a workload (the three single-layer workloads share seed 0)."""
+    if workload in ("single_b1", "batch_sweep", "routing_stress"):
         return 0
-    if config == 4:
+    if workload == "decode_step":
         return layer
-    if config == 5:
+    if workload == "wide_layers":
         return 5000 + layer
-    raise ValueError(config)
+    raise ValueError(workload)
 
 
-def routing_seed(config: int, B: int, routing: str = "uniform", layer: int = 0) -> int:
+def routing_seed(workload: str, B: int, routing: str = "uniform", layer: int = 0) -> int:
     """Seed of the activation/routing stream; iteration r of that stream uses spawn key r."""
-    if config == 1:
+    if workload == "single_b1":
         return 0
-    if config == 2:
+    if workload == "batch_sweep":
         return 1000 + B
-    if config == 3:
+    if workload == "routing_stress":
         return _ROUTE_BASE[routing]
-    if config == 4:
+    if workload == "decode_step":
         return 4000 + layer
-    if config == 5:
+    if workload == "wide_layers":
         return 5000 + layer
-    raise ValueError(config)
+    raise ValueError(workload)

@@ -23,7 +23,7 @@ def test_layer_bytes_formula(B):
     """D distinct experts' rows and scales + x read and y written (2H each per token)
     + h written and read (2 * 2I per slot) + ids read twice and a router weight (12 B per slot)."""
     H, I, k = 2048, 768, 8
-    ids, _ = mi.route_uniform(mi.routing_seed(2, B), B, 128, k)
+    ids, _ = mi.route_uniform(mi.routing_seed("batch_sweep", B), B, 128, k)
     d = bench.layer_bytes(ids, H, I, k)
     D = len(set(ids.ravel().tolist()))
     assert d["distinct"] == D

@@ -84,19 +84,19 @@ def test_conventional_small_shapes(dev, shape):
 @pytest.fixture(scope="module")
 def s1(dev):
     s = mi.SHAPES["S1"]
-    L = mi.make_layer(mi.layer_seed(1), s["H"], s["I"], s["E"])
+    L = mi.make_layer(mi.layer_seed("single_b1"), s["H"], s["I"], s["E"])
     return L, _weights(L, dev)
 
 
 @pytest.mark.parametrize("B", [1, 8, 32])
-def test_conventional_config2(dev, s1, B):
+def test_conventional_batch_sweep(dev, s1, B):
     L, W = s1
-    seed = mi.routing_seed(2, B)
+    seed = mi.routing_seed("batch_sweep", B)
     x = mi.make_x(seed, B, L.H)
     ids, w = mi.route_uniform(seed, B, L.E, 8)
     y = run_conventional(W, x, ids, w, dev, B, L.H, L.I, L.E, 8)
     ref = oracle.conventional(x, ids, w, L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
-    check_loose(y, ref, f"conventional config2 B={B}")
+    check_loose(y, ref, f"conventional batch sweep B={B}")
 
 
 def test_conventional_invalid_ids_give_nan(dev, s1):

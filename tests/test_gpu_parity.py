@@ -235,58 +235,58 @@ def test_duplicate_ids_within_a_token(dev, small_layers, variant):
 @pytest.fixture(scope="module")
 def s1(dev):
     s = mi.SHAPES["S1"]
-    return DevLayer(mi.make_layer(mi.layer_seed(1), s["H"], s["I"], s["E"]), dev)
+    return DevLayer(mi.make_layer(mi.layer_seed("single_b1"), s["H"], s["I"], s["E"]), dev)
 
 
-def _full(D, config, B, routing, dev, it=0, variants=(None,)):
-    seed = mi.routing_seed(config, B, routing)
+def _full(D, workload, B, routing, dev, it=0, variants=(None,)):
+    seed = mi.routing_seed(workload, B, routing)
     x = mi.make_x(seed, B, D.H, it=it)
     ids, w = mi.make_routing(routing, seed, B, D.E, 8, it=it)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
     for v in variants:
         h, y = run_gpu(D, x, ids, w, dev, variant=v)
-        check(h, y, h_ref, y_ref, B, 8, f"config{config} B={B} {routing} variant={v}")
+        check(h, y, h_ref, y_ref, B, 8, f"{workload} B={B} {routing} variant={v}")
 
 
-def test_config1_single_layer_b1(dev, s1):
-    _full(s1, 1, 1, "uniform", dev)
+def test_single_layer_b1(dev, s1):
+    _full(s1, "single_b1", 1, "uniform", dev)
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
-def test_config2_batch_sweep(dev, s1, B):
-    _full(s1, 2, B, "uniform", dev, variants=BOTH)
+def test_batch_sweep(dev, s1, B):
+    _full(s1, "batch_sweep", B, "uniform", dev, variants=BOTH)
 
 
 @pytest.mark.parametrize("routing", ["zipf", "adversarial", "contiguous"])
-def test_config3_routing_stress(dev, s1, routing):
-    _full(s1, 3, 32, routing, dev, variants=BOTH)
+def test_routing_stress_b32(dev, s1, routing):
+    _full(s1, "routing_stress", 32, routing, dev, variants=BOTH)
 
 
 @pytest.mark.parametrize("layer", [1, 47])
-def test_config4_layers(dev, layer):
+def test_decode_step_layers(dev, layer):
     s = mi.SHAPES["S1"]
-    D = DevLayer(mi.make_layer(mi.layer_seed(4, layer), s["H"], s["I"], s["E"]), dev)
+    D = DevLayer(mi.make_layer(mi.layer_seed("decode_step", layer), s["H"], s["I"], s["E"]), dev)
     for B in (1, 8, 32):
-        seed = mi.routing_seed(4, B, layer=layer)
+        seed = mi.routing_seed("decode_step", B, layer=layer)
         x = mi.make_x(seed, B, D.H)
         ids, w = mi.route_uniform(seed, B, D.E, 8)
         h, y = run_gpu(D, x, ids, w, dev)
         h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
-        check(h, y, h_ref, y_ref, B, 8, f"config4 layer={layer} B={B}")
+        check(h, y, h_ref, y_ref, B, 8, f"decode step layer={layer} B={B}")
 
 
-def test_config5_wide_layer_sampled_tokens(dev):
+def test_wide_layer_sampled_tokens(dev):
     s = mi.SHAPES["S2"]
-    D = DevLayer(mi.make_layer(mi.layer_seed(5, 0), s["H"], s["I"], s["E"]), dev)
+    D = DevLayer(mi.make_layer(mi.layer_seed("wide_layers", 0), s["H"], s["I"], s["E"]), dev)
     for B in (1, 16, 32, 64):
-        seed = mi.routing_seed(5, B, layer=0)
+        seed = mi.routing_seed("wide_layers", B, layer=0)
         x = mi.make_x(seed, B, D.H)
         ids, w = mi.route_uniform(seed, B, D.E, 8)
         toks = sorted({0, B // 2, B - 1})
         h_ref, y_ref = oracle.layer(x[toks], ids[toks], w[toks], *D.host())
         for v in BOTH:
             h, y = run_gpu(D, x, ids, w, dev, variant=v)
-            check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"config5 B={B} tokens={toks} variant={v}")
+            check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"wide layer B={B} tokens={toks} variant={v}")
 
 
 # --------------------------------------------------------------- properties

@@ -85,7 +85,7 @@ def test_route_kernel_special_values(dev):
 def test_route_workload_logits(dev):
     """The 128-expert, top-8 router at B = 1..64 on the workload's N(0,1) logits."""
     for B in (1, 8, 32, 64):
-        logits = mi.router_logits(mi.routing_seed(1, B), B, 128)
+        logits = mi.router_logits(mi.routing_seed("single_b1", B), B, 128)
         ids, w = run_route(logits, 8, dev)
         check_route(ids, w, logits, 8, f"route workload B={B}")
 
@@ -135,7 +135,7 @@ def test_routed_gate_up_small(dev, shape):
 @pytest.fixture(scope="module")
 def s1(dev):
     s = mi.SHAPES["S1"]
-    return DevLayer(mi.make_layer(mi.layer_seed(1), s["H"], s["I"], s["E"]), dev)
+    return DevLayer(mi.make_layer(mi.layer_seed("single_b1"), s["H"], s["I"], s["E"]), dev)
 
 
 @pytest.mark.parametrize("B", [1, 8, 32])
@@ -144,7 +144,7 @@ def test_routed_gate_up_workload(dev, s1, B):
     built-in choice (the fused prologue at 1 token; the router kernel, then the
     per-slot kernel at 8 and the grouped kernel at 32) and, at 8 and 32 tokens,
     the fused per-slot kernel too."""
-    seed = mi.routing_seed(1, B)
+    seed = mi.routing_seed("single_b1", B)
     x = mi.make_x(seed, B, s1.H)
     logits = mi.router_logits(seed, B, s1.E)
     check_routed(s1, x, logits, 8, run_routed(s1, x, logits, 8, dev), f"routed workload B={B}")

@@ -83,7 +83,7 @@ def test_layer_independent_of_thread_count():
         assert np.array_equal(getattr(a, n), getattr(b, n))
 
 
-def test_config_table():
-    assert mi.CONFIGS[2]["batches"] == (1, 2, 4, 8, 16, 32)
+def test_workload_table():
+    assert mi.WORKLOADS["batch_sweep"]["batches"] == (1, 2, 4, 8, 16, 32)
     assert mi.SHAPES["S1"] == dict(H=2048, I=768, E=128, k=8)
-    assert mi.layer_seed(1) == 0 and mi.routing_seed(2, 32) == 1032
+    assert mi.layer_seed("single_b1") == 0 and mi.routing_seed("batch_sweep", 32) == 1032

@@ -96,7 +96,7 @@ def test_route_properties_on_the_workload(orc):
     dropped one, weights positive, non-increasing and summing to one; and the
     input generator's own top-k (argsort + FP32 softmax) agrees."""
     B, E, k = 64, 128, 8
-    logits = mi.router_logits(mi.routing_seed(2, B), B, E)
+    logits = mi.router_logits(mi.routing_seed("batch_sweep", B), B, E)
     ids, w = orc.route(logits, k)
     for b in range(B):
         kept = set(ids[b].tolist())
@@ -105,7 +105,7 @@ def test_route_properties_on_the_workload(orc):
         assert min(logits[b, ids[b]]) >= max(dropped)
     assert np.all(w > 0) and np.all(np.diff(w, axis=1) <= 0)
     np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-15)
-    gi, gw = mi.route_uniform(mi.routing_seed(2, B), B, E, k)
+    gi, gw = mi.route_uniform(mi.routing_seed("batch_sweep", B), B, E, k)
     assert np.array_equal(ids, gi)
     np.testing.assert_allclose(w, gw, rtol=2e-7)
 
