@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
   // unit loop by the index build's barriers
   for (int i = tid; i < slots * (RO + 1); i += NT) contrib[i] = 0.0f;
   if (tid == 0) *next_unit = NW;   // units 0 .. NW-1 go to wavefronts 0 .. NW-1
-  const SlotIndex si = build_slot_index<NT>(lds, ids, slots, E, k, kDownGroupedUnitSlots);
+  const SlotIndex si = build_slot_index<NT, false>(lds, ids, slots, E, k, kDownGroupedUnitSlots);
 
   const int nblk = I >> 5;
   uint32_t off[NP];

@@ -81,7 +81,7 @@ void moe_gate_up_expert_grouped_w64(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  const SlotIndex si = build_slot_index<256>(lds, ids, slots, E, k, grouped_unit_slots(H));
+  const SlotIndex si = build_slot_index<256, true>(lds, ids, slots, E, k, grouped_unit_slots(H));
   uint8_t* xs = lds + slot_index_lds_bytes(E, slots);   // M rows of x, 2H bytes each, 1 KB-padded
   const rsrc_t idr = make_rsrc(ids, (uint64_t)slots * 4);
 
