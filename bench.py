@@ -122,6 +122,8 @@ def kernel_source_hash() -> str:
     for f in sorted(os.listdir(d)):   # every kernel source and header of the library
         if f.endswith((".hpp", ".hip")):
             h.update(f.encode() + b"\0" + open(os.path.join(d, f), "rb").read())
+    # and the compiler flags they are built with
+    h.update(b"build.py\0" + open(os.path.join(ROOT, "moe_gate_up_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

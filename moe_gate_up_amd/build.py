@@ -18,6 +18,10 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into SGPRs when the wave starts: one scalar
+    # load round trip less before a kernel's first (dependent) loads; at one
+    # token per step that is 2 % of the layer (12.4 -> 12.1 us on MI355X)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
 ]
 

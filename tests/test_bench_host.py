@@ -62,6 +62,20 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("gate_up") is None
 
 
+def test_source_hash_covers_the_build_flags(tmp_path, monkeypatch):
+    """A change of the compiler flags changes the hash (and so voids stored counters)."""
+    h = bench.kernel_source_hash()
+    root = tmp_path
+    (root / "moe_gate_up_amd").mkdir()
+    os.symlink(os.path.join(bench.ROOT, "moe_gate_up_amd", "csrc"), root / "moe_gate_up_amd" / "csrc")
+    src = open(os.path.join(bench.ROOT, "moe_gate_up_amd", "build.py")).read()
+    (root / "moe_gate_up_amd" / "build.py").write_text(src)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    assert bench.kernel_source_hash() == h
+    (root / "moe_gate_up_amd" / "build.py").write_text(src + "\n# -O2\n")
+    assert bench.kernel_source_hash() != h
+
+
 def test_source_hash_covers_every_kernel_source():
     csrc = os.path.join(bench.ROOT, "moe_gate_up_amd", "csrc")
     files = [f for f in os.listdir(csrc) if f.endswith((".hpp", ".hip"))]
