@@ -231,6 +231,30 @@ def test_duplicate_ids_within_a_token(dev, small_layers, variant):
     check(h, y, h_ref, y_ref, B, k, f"duplicates variant={variant}")
 
 
+@pytest.mark.parametrize("variant", FAMILIES, ids=["per_slot", "grouped"])
+def test_one_expert_over_several_work_units(dev, small_layers, variant):
+    """Every token routes its first slot to expert 3: 40 slots of one expert, more
+    than one work unit holds (16 in gate/up, 8 in down), so the expert's slots are
+    cut into several units that different workgroups process -- every workgroup
+    must cut them the same way.  Checked against the oracle, and twice for
+    bit-identical results."""
+    shape = (3, 2048, 96, 16, 8)
+    _, H, I, E, k = shape
+    B = 40
+    D = small_layers[shape]
+    x = mi.make_x(9, B, H)
+    ids, w = mi.route_uniform(9, B, E, k)
+    for b in range(B):
+        row = [e for e in ids[b] if e != 3][: k - 1]
+        ids[b] = [3] + row + [e for e in range(E) if e != 3 and e not in row][: k - 1 - len(row)]
+    assert (ids == 3).sum() == B and all(len(set(r)) == k for r in ids.tolist())
+    h, y = run_gpu(D, x, ids, w, dev, variant=variant)
+    h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
+    check(h, y, h_ref, y_ref, B, k, f"one expert over several units, variant={variant}")
+    h2, y2 = run_gpu(D, x, ids, w, dev, variant=variant)
+    assert np.array_equal(h, h2) and np.array_equal(y, y2)
+
+
 # --------------------------------------------------------------- full-size workloads
 @pytest.fixture(scope="module")
 def s1(dev):
