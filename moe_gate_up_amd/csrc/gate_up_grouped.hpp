@@ -11,15 +11,17 @@
 // average routed expert serves 2.3 slots, and those repeat reads (L2 hits)
 // occupy the vector-memory pipeline that the weight stream needs.
 //
-// The grid is persistent: about as many workgroups as the chip holds at once,
-// each taking pairs of work items round-robin.  Every
+// The grid is persistent: at most 2048 workgroups (about two per slot the
+// chip holds at once), each taking pairs of work items round-robin.  Every
 // workgroup first indexes the B*k <= 1024 slots by expert in LDS
 // (slot_index.hpp), which yields the routed experts and each one's slots, cut
 // into work units of at most min(4M, 16) slots (four fillings of the 32 KB
 // LDS staging area of M x rows), so that an expert shared by many tokens is
-// spread over
-// several workgroups while an expert with a handful of slots is one unit (its
-// rows read once).  Unrouted experts produce no work.  A work item is a work
+// spread over several workgroups while an expert with a handful of slots is
+// one unit (its rows read once).  Since one expert's units go to different
+// workgroups, every workgroup must cut them alike: the index puts the slots
+// of such experts in slot order (STABLE).  Unrouted experts produce no
+// work.  A work item is a work
 // unit times a group of 4R neurons:
 //  1. each wavefront issues its R gate and R up rows (1 KB-contiguous passes
 //     as in the per-slot kernel) and their E8M0 scales;

@@ -183,10 +183,12 @@ bool grouped_allowed(int nch, int r, long long slots, int E) {
          slots <= moe::kGroupedMaxSlots && E <= moe::kGroupedMaxExperts;
 }
 
-// Persistent grid of at most 2048 workgroups (8 per CU of MI355X's 256;
-// 1024 to 2560 measured within 4 %) and never more than the largest possible
-// number of work item pairs; dynamic LDS: per-expert counters, sorted slots
-// and staged activations.
+// Persistent grid of at most 2048 workgroups (8 per CU of MI355X's 256, 4 of
+// which fit at once) and never more than the largest possible number of work
+// item pairs; dynamic LDS: the slot index and the staged activations.  From a
+// graph-timed sweep at 32 and 64 tokens: 1024 workgroups are ~3 % slower;
+// 3072-4096 are up to 2 % faster under uniform routing but up to 13 % slower
+// under Zipf routing, where hot experts make some work items much longer.
 #ifndef MOE_GROUPED_BLOCKS
 #define MOE_GROUPED_BLOCKS 2048
 #endif
@@ -248,10 +250,13 @@ GateUpLaunch pick_grouped(int nch, int r) {
 // Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
 // experts, top-8, uniform routing).  While the average routed expert serves
 // few slots, the per-slot kernel wins: it needs no sort and its grid has no
-// per-workgroup setup (16 tokens, H = 2048: 47.8 vs 52.8 us).  From two slots
-// per expert on (B*k >= 2E) the expert-grouped kernel reads each routed row
-// once and wins (32 tokens: 71.5 vs 77.5 us at H = 2048, 268 vs 300 us at
-// H = 4096; 64 tokens: 95 vs 117 and 374 vs 445 us).
+// per-workgroup setup (16 tokens, H = 2048: 48.2 vs 52.4 us; 24 tokens: 62.6
+// vs 64.3).  From two slots per expert on (B*k >= 2E) the expert-grouped
+// kernel reads each routed row once and wins (32 tokens: 70.8 vs 77.4 us at
+// H = 2048, 268 vs 300 us at H = 4096; 64 tokens: 95 vs 117 and 374 vs
+// 445 us).  Skewed routing favours it earlier (24 tokens, Zipf: 49.5 vs
+// 52.9 us), and so does H = 4096 (24 tokens: 238 vs 249 us); the threshold
+// stays at the uniform H = 2048 crossover.
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
