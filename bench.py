@@ -151,7 +151,9 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="device copies of the layer weights, cycled per step")
     ap.add_argument("--routings", type=int, default=64, help="pre-generated routings, cycled per step")
     ap.add_argument("--sweep", default="1,2,4,8,16,32", help="batch sizes for the sweep ('' to skip)")
-    ap.add_argument("--sweep-steps", type=int, default=100)
+    # per-step time settles after ~100 steps of a replay (50: +5.6 %, 100: +1.5 %,
+    # 200: +0.2 % over 400-800 steps at B=32 on MI355X); 200 is within noise
+    ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the routing-stress, 48-layer and wide-shape runs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
