@@ -104,11 +104,22 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     expert's rows once (section "Warp decode and Composer training": the
  *     regime where several tokens share an expert).  Same outputs; requires
  *     B*k <= 1024 and E <= 1024.
- * The plain call takes the grouped variant once B*k >= 2E (an average of two
- * or more slots per expert) and the limits allow it, else the per-slot one:
- * the faster of the two in each measured configuration. */
+ *   MOE_GATE_UP_EXPERT_GROUPED_MFMA: the same grouping with the dot products
+ *     on the matrix cores (v_mfma_f32_16x16x32_bf16): a workgroup takes 16
+ *     neurons of one routed expert for up to 16 of its slots, streaming the
+ *     rows and activations through LDS in 512-element chunks; the E8M0 scale
+ *     is folded into the E4M3 -> bf16 conversion.  Same outputs within the
+ *     same tolerance; requires H a multiple of 2048 up to 8192, B*k <= 1024,
+ *     E <= 1024, and s_gate, s_up 16-byte aligned (MOE_ERR_ALIGN otherwise;
+ *     rows_per_wave must be 0 or 16).
+ * The plain call takes the matrix-core variant from four slots per expert on
+ * (B*k >= 4E), or from two at H >= 4096, when its limits allow (with
+ * unaligned scales it takes the vector-unit grouped variant instead), the
+ * vector-unit grouped one from two slots per expert on (B*k >= 2E), else the
+ * per-slot one: the fastest in each measured configuration. */
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
+#define MOE_GATE_UP_EXPERT_GROUPED_MFMA 3
 
 /* Kernel variants of the down call.
  *   MOE_DOWN_PER_TOKEN: one wavefront per (R output dimensions, token) --

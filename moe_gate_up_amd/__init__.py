@@ -27,6 +27,7 @@ MOE_ERR_ALIAS = -5
 MOE_ERR_ARG = -6
 MOE_GATE_UP_PER_SLOT = 1
 MOE_GATE_UP_EXPERT_GROUPED = 2
+MOE_GATE_UP_EXPERT_GROUPED_MFMA = 3
 MOE_DOWN_PER_TOKEN = 1
 MOE_DOWN_EXPERT_GROUPED = 2
 

@@ -11,6 +11,7 @@
 #include "conventional.hpp"
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
+#include "gate_up_grouped_mfma.hpp"
 #include "peak.hpp"
 #include "router.hpp"
 
@@ -247,6 +248,37 @@ GateUpLaunch pick_grouped(int nch, int r) {
   return nullptr;
 }
 
+// Matrix-core grouped kernel: a persistent grid of one resident round of
+// workgroups (two per CU while the LDS footprint allows, on MI355X's 256 CUs;
+// a sweep of 384 to 1024 workgroups at 32 and 64 tokens found exactly one
+// round fastest, partial rounds up to 25 % slower); dynamic LDS: the slot
+// index, two chunk buffers and the item's scale codes.
+constexpr long long kMfmaCus = 256;
+constexpr int kLdsPerCu = 160 * 1024;
+bool mfma_allowed(int H, long long slots, int E) {
+  return H % 2048 == 0 && H <= 8192 && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts;
+}
+
+long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
+                      const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
+                      int k, const RouteIO* ro) {
+  const long long slots = (long long)B * k;   // work units (<= slots) x groups of 16 neurons
+  const long long items_max = slots * (long long)((I + moe::kMfmaRows - 1) / moe::kMfmaRows);
+  const int lds = moe::mfma_lds_bytes(E, (int)slots, H);
+  const long long per_cu = kLdsPerCu / lds > 2 ? 2 : (kLdsPerCu / lds < 1 ? 1 : kLdsPerCu / lds);
+  const long long blocks = items_max < kMfmaCus * per_cu ? items_max : kMfmaCus * per_cu;
+  if (!go) return blocks;
+  if (ro) {
+    launch_route(st, *ro, B, E, k);
+    ids = ro->ids;
+  }
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_gate_up_grouped_mfma_w64),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipLaunchKernelGGL(moe::moe_gate_up_grouped_mfma_w64, dim3((unsigned)blocks), dim3(256), (unsigned)lds, st,
+                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k);
+  return blocks;
+}
+
 // Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
 // experts, top-8, uniform routing).  While the average routed expert serves
 // few slots, the per-slot kernel wins: it needs no sort and its grid has no
@@ -257,9 +289,18 @@ GateUpLaunch pick_grouped(int nch, int r) {
 // 445 us).  Skewed routing favours it earlier (24 tokens, Zipf: 49.5 vs
 // 52.9 us), and so does H = 4096 (24 tokens: 238 vs 249 us); the threshold
 // stays at the uniform H = 2048 crossover.
+//
+// From four slots per expert on (B*k >= 4E), and from two at H >= 4096, the
+// expert-grouped product runs on the matrix cores: 64 tokens at H = 2048
+// 82.0 vs 93.0 us, at H = 4096 300 vs 360 us; 32 tokens at H = 4096 255 vs
+// 269 us, at H = 2048 71.2 vs 70.3 (the vector-unit kernel keeps that one).
+// Under Zipf routing the matrix-core kernel wins already at 32 tokens, H =
+// 2048 (55.2 vs 59.6 us); the table follows uniform routing.
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
+  if ((slots >= 4LL * E || (slots >= 2LL * E && H >= 4096)) && mfma_allowed(H, slots, E))
+    return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
   if (slots >= 2LL * E && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;
 }
@@ -282,6 +323,10 @@ GateUpLaunch gate_up_launcher(int& variant, int nch, int& rows, int B, int H, in
   if (variant == MOE_GATE_UP_EXPERT_GROUPED) {
     if (rows == 0) rows = grouped_default_rows(H);
     return grouped_allowed(nch, rows, (long long)B * k, E) ? pick_grouped(nch, rows) : nullptr;
+  }
+  if (variant == MOE_GATE_UP_EXPERT_GROUPED_MFMA) {
+    if (rows == 0) rows = moe::kMfmaRows;
+    return rows == moe::kMfmaRows && mfma_allowed(H, (long long)B * k, E) ? launch_mfma : nullptr;
   }
   return nullptr;
 }
@@ -343,8 +388,16 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
     rt.fuse = variant == MOE_GATE_UP_PER_SLOT && E <= moe::kRouteFusedMaxExperts;
     ro = &rt;
   }
+  const bool asked = variant != 0;
   GateUpLaunch fn = gate_up_launcher(variant, nch, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
+  if (variant == MOE_GATE_UP_EXPERT_GROUPED_MFMA && (!aligned(sg, 16) || !aligned(su, 16))) {
+    if (asked) return MOE_ERR_ALIGN;   // the matrix-core kernel copies 16-byte pieces of the scales
+    variant = MOE_GATE_UP_EXPERT_GROUPED;   // the table's choice: fall back
+    rows = 0;
+    fn = gate_up_launcher(variant, nch, rows, B, H, I, E, k);
+    if (!fn) return MOE_ERR_ARG;
+  }
   const long long blocks = fn(false, nullptr, x, ids, wg, sg, wu, su, h, B, H, I, E, k, ro);
   if (blocks * kWavesPerBlock >= (1LL << 31)) return MOE_ERR_SHAPE;
   (void)hipGetLastError();

@@ -93,6 +93,10 @@ def test_null_pointer_errors():
 def test_alignment_errors():
     for name in ("x", "wg", "wu", "h"):
         assert gu(**{name: A + 8 * S + 8}) == mg.MOE_ERR_ALIGN, name
+    # the matrix-core kernel copies 16-byte pieces of the scale tensors: asked for
+    # explicitly it needs them 16-byte aligned
+    for name in ("sg", "su"):
+        assert gu(rows=0, variant=mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA, **{name: A + 8 * S + 4}) == mg.MOE_ERR_ALIGN, name
     assert gu(ids=A + 8 * S + 2) == mg.MOE_ERR_ALIGN
     for name in ("h", "wd"):
         assert dn(**{name: A + 8 * S + 8}) == mg.MOE_ERR_ALIGN, name
@@ -155,14 +159,21 @@ def test_conventional_path_arguments():
 def test_plans():
     for B in (1, 8, 16, 32, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
-        assert r in (1, 2, 4, 8)
         if v == mg.MOE_GATE_UP_PER_SLOT:   # one wavefront per (tile, slot)
+            assert r in (1, 2, 4, 8)
             assert g == -(-((768 + r - 1) // r) * B * 8 // 4)
-        else:                              # persistent: <= 2048 workgroups, <= the possible work items
-            assert v == mg.MOE_GATE_UP_EXPERT_GROUPED
+        elif v == mg.MOE_GATE_UP_EXPERT_GROUPED:   # persistent: <= 2048 workgroups, <= the possible work items
+            assert r in (1, 2, 4, 8)
             assert g == min(2048, -(-(B * 8 * -(-768 // (4 * r))) // 2))   # items taken in pairs
-        # grouped once the batch averages two or more slots per expert
-        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (B * 8 >= 2 * 128)
+        else:                              # matrix cores: one resident round, two workgroups per CU
+            assert v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA and r == 16 and g == 512
+        # grouped from two slots per expert on, on the matrix cores from four
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (2 * 128 <= B * 8 < 4 * 128)
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (B * 8 >= 4 * 128)
+    # H = 4096: the matrix cores from two slots per expert on; H not a multiple of 2048: never
+    assert mg.moe_decode_gate_up_plan(32, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
+    assert mg.moe_decode_gate_up_plan(16, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    assert mg.moe_decode_gate_up_plan(64, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
     for B in (1, 8, 16, 32, 64):
