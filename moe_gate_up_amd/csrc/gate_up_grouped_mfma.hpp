@@ -19,8 +19,8 @@
 // while chunk c is multiplied.  Every lane's 16-byte piece lands at a fixed
 // LDS position (16 x lane), so the pieces are swizzled on the way in: lane l
 // fetches piece l ^ (row mod 16) of a weight row and piece l ^ 2 (token mod
-// 16) of an activation row, which makes the MFMA operand reads from LDS free
-// of bank conflicts.  The 4 wavefronts split a chunk's eight 64-element
+// 16) -- two times the token's index mod 16 -- of an activation row, which
+// makes the MFMA operand reads from LDS free of bank conflicts.  The 4 wavefronts split a chunk's eight 64-element
 // tiles; in a tile, lane (r, q) (r = lane mod 16, q = lane / 16) takes
 // elements 16 q .. 16 q + 15 of row r and of token r, the first 8 for one
 // MFMA and the last 8 for another (the same K order on both operands).
@@ -33,10 +33,13 @@
 // sum.  NaN scale codes and E4M3 NaN codes give NaN outputs.
 //
 // After the last chunk each wavefront's 16 x 16 gate and up partial sums go
-// to LDS and threads (n, t) add the 4 partials in wavefront order (a fixed
-// order) and write h = bf16(SiLU(g) * u).  Items go out round-robin over the
-// persistent grid.  Limits: H a multiple of 512 up to 8192, B*k <= 1024,
-// E <= 1024.
+// to LDS (the chunk buffer the last chunk leaves free) and threads (n, t) add
+// the 4 partials in wavefront order (a fixed order) and write
+// h = bf16(SiLU(g) * u).  Items go out round-robin over a grid of one
+// resident round (LDS: under 80 KB for the decode shapes, two workgroups per
+// CU).  Limits: H a multiple of 2048 up to 8192 (an item's scale codes are
+// copied in whole KB pieces, one matrix per piece), B*k <= 1024, E <= 1024,
+// scale tensors 16-byte aligned.
 #pragma once
 
 #include "slot_index.hpp"
