@@ -436,8 +436,9 @@ def main():
     gu_variant = mg.moe_decode_gate_up_plan(B, H, I, E, k)[0]
     roof = {
         "bound": "hbm",
-        "kernel": "moe_gate_up_expert_grouped_w64" if gu_variant == mg.MOE_GATE_UP_EXPERT_GROUPED
-        else "moe_gate_up_3d_batched_w64",
+        "kernel": {mg.MOE_GATE_UP_PER_SLOT: "moe_gate_up_3d_batched_w64",
+                   mg.MOE_GATE_UP_EXPERT_GROUPED: "moe_gate_up_expert_grouped_w64",
+                   mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA: "moe_gate_up_grouped_mfma_w64"}[gu_variant],
         "achieved": round(kern["gate_up_GBps"], 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",

@@ -112,11 +112,12 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     same tolerance; requires H a multiple of 2048 up to 8192, B*k <= 1024,
  *     E <= 1024, and s_gate, s_up 16-byte aligned (MOE_ERR_ALIGN otherwise;
  *     rows_per_wave must be 0 or 16).
- * The plain call takes the matrix-core variant from four slots per expert on
- * (B*k >= 4E), or from two at H >= 4096, when its limits allow (with
- * unaligned scales it takes the vector-unit grouped variant instead), the
- * vector-unit grouped one from two slots per expert on (B*k >= 2E), else the
- * per-slot one: the fastest in each measured configuration. */
+ * The plain call takes the matrix-core variant from 1.5 slots per expert on
+ * (2*B*k >= 3E), or from half a slot at H >= 4096 (2*B*k >= E), when its
+ * limits allow (with unaligned scales it takes the vector-unit grouped
+ * variant instead); where they do not, the vector-unit grouped one from two
+ * slots per expert on (B*k >= 2E); else the per-slot one: the fastest in each
+ * measured configuration. */
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
 #define MOE_GATE_UP_EXPERT_GROUPED_MFMA 3

@@ -76,10 +76,9 @@ __device__ __forceinline__ bf16x8_t e4m3x8_scaled(uint32_t lo, uint32_t hi, floa
   return r;
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  const v4u t = {a, b, c, d};
-  return __builtin_bit_cast(bf16x8_t, t);
+// Byte address in LDS of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Nonzero iff a byte of v is an E8M0 code in [247, 255].
@@ -162,8 +161,9 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
     for (int c = 0; c < n_chunks; ++c) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wavefront's copies of chunk c (and the scales)
       __syncthreads();                            // everyone's; and everyone is done with chunk c - 1
-      if (c + 1 < n_chunks) copy_chunk(c + 1);
-      if (c == 0) {   // codes above 246 anywhere in the item's rows (a wave-wide check)
+      // codes above 246 anywhere in the item's rows (a wave-wide check), read
+      // before the copies of chunk 1 are issued so that these reads wait for nothing
+      if (c == 0) {
         uint32_t any = 0;
         for (int i = lane * 16; i < 2 * kMfmaRows * nblk; i += 1024) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(scl + i);
@@ -181,27 +181,60 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
           du = mu > kMfmaSafeScale ? mu - kMfmaSafeScale : 0;
         }
       }
+      if (c + 1 < n_chunks) copy_chunk(c + 1);
       const uint8_t* wb = buf + (c & 1) * kMfmaBufBytes;
       const uint8_t* xb = wb + kMfmaWBytes;
+      // This wavefront's operands of chunk c: its tiles tl = 2w and 2w + 1 (64
+      // elements each).  Lane (lr, lq) takes the 16-byte piece 4 tl + lq of gate
+      // row lr and of up row lr (8192 bytes further), the pieces 8 tl + 2 lq and
+      // + 1 of token tc's activations, and the E8M0 codes of the gate and up
+      // blocks those pieces belong to (the second tile's: 2 bytes further).
+      // The reads are one asm block with its own wait: as plain loads the
+      // compiler, which cannot tell them from the copies of chunk c + 1 into
+      // the other buffer, waited for those copies first, and nothing overlapped.
+      static_assert(kMfmaRows * kMfmaChunk == 8192 && kMfmaChunk / 32 / 8 == 2, "offsets in the asm below");
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+      v4u ag0, au0, xa0, xb0, ag1, au1, xa1, xb1;
+      uint32_t cg0, cu0, cg1, cu1;
+      {
+        const int tl0 = 2 * w;
+        const uint32_t pa0 = lds_addr(wb + lr * kMfmaChunk + 16 * ((4 * tl0 + lq) ^ lr));
+        const uint32_t pa1 = lds_addr(wb + lr * kMfmaChunk + 16 * ((4 * tl0 + 4 + lq) ^ lr));
+        const uint32_t px0 = lds_addr(xb + tc * 1024 + 16 * ((8 * tl0 + 2 * lq) ^ (2 * (tc & 15))));
+        const uint32_t px1 = lds_addr(xb + tc * 1024 + 16 * ((8 * tl0 + 8 + 2 * lq) ^ (2 * (tc & 15))));
+        const int blk = c * (kMfmaChunk / 32) + 2 * tl0 + (lq >> 1);
+        const uint32_t psg = lds_addr(scl + lr * nblk + blk), psu = lds_addr(scl + (kMfmaRows + lr) * nblk + blk);
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:8192\n\t"
+            "ds_read_b128 %2, %14\n\t"
+            "ds_read_b128 %3, %14 offset:16\n\t"
+            "ds_read_b128 %4, %13\n\t"
+            "ds_read_b128 %5, %13 offset:8192\n\t"
+            "ds_read_b128 %6, %15\n\t"
+            "ds_read_b128 %7, %15 offset:16\n\t"
+            "ds_read_u8 %8, %16\n\t"
+            "ds_read_u8 %9, %17\n\t"
+            "ds_read_u8 %10, %16 offset:2\n\t"
+            "ds_read_u8 %11, %17 offset:2\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(ag0), "=&v"(au0), "=&v"(xa0), "=&v"(xb0), "=&v"(ag1), "=&v"(au1), "=&v"(xa1), "=&v"(xb1),
+              "=&v"(cg0), "=&v"(cu0), "=&v"(cg1), "=&v"(cu1)
+            : "v"(pa0), "v"(pa1), "v"(px0), "v"(px1), "v"(psg), "v"(psu)
+            : "memory");
+      }
+      const v4u a_g[2] = {ag0, ag1}, a_u[2] = {au0, au1}, b0[2] = {xa0, xa1}, b1[2] = {xb0, xb1};
+      const int cg[2] = {(int)cg0, (int)cg1}, cu[2] = {(int)cu0, (int)cu1};
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int tl = 2 * w + tt;                // 64-element tile of the chunk
-        const int piece = 4 * tl + lq;            // 16-byte piece of the 512-byte row chunk
-        const u32x4 a_g = *reinterpret_cast<const u32x4*>(wb + lr * kMfmaChunk + 16 * (piece ^ lr));
-        const u32x4 a_u = *reinterpret_cast<const u32x4*>(wb + (kMfmaRows + lr) * kMfmaChunk + 16 * (piece ^ lr));
-        const int xp = (8 * tl + 2 * lq) ^ (2 * (tc & 15));   // pieces xp, xp + 1 of the token's 1 KB
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(xb + tc * 1024 + 16 * xp);
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + tc * 1024 + 16 * (xp + 1));
-        const int blk = c * (kMfmaChunk / 32) + 2 * tl + (lq >> 1);
-        const int cg = scl[lr * nblk + blk], cu = scl[(kMfmaRows + lr) * nblk + blk];
-        const float sgf = __builtin_bit_cast(float, (uint32_t)(cg == 255 ? 255 : max(cg - dg, 0)) << 23);
-        const float suf = __builtin_bit_cast(float, (uint32_t)(cu == 255 ? 255 : max(cu - du, 0)) << 23);
-        const bf16x8_t x0 = as_bf16x8(b0.v[0], b0.v[1], b0.v[2], b0.v[3]);
-        const bf16x8_t x1 = as_bf16x8(b1.v[0], b1.v[1], b1.v[2], b1.v[3]);
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_g.v[0], a_g.v[1], sgf), x0, accg, 0, 0, 0);
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_g.v[2], a_g.v[3], sgf), x1, accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_u.v[0], a_u.v[1], suf), x0, accu, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_u.v[2], a_u.v[3], suf), x1, accu, 0, 0, 0);
+        const float sgf = __builtin_bit_cast(float, (uint32_t)(cg[tt] == 255 ? 255 : max(cg[tt] - dg, 0)) << 23);
+        const float suf = __builtin_bit_cast(float, (uint32_t)(cu[tt] == 255 ? 255 : max(cu[tt] - du, 0)) << 23);
+        const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, b0[tt]);
+        const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, b1[tt]);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_g[tt][0], a_g[tt][1], sgf), x0, accg, 0, 0, 0);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_g[tt][2], a_g[tt][3], sgf), x1, accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_u[tt][0], a_u[tt][1], suf), x0, accu, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_scaled(a_u[tt][2], a_u[tt][3], suf), x1, accu, 0, 0, 0);
       }
     }
     // lane l holds rows 4 (l / 16) + j of column l % 16

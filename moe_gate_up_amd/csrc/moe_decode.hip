@@ -280,26 +280,23 @@ long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids
 }
 
 // Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
-// experts, top-8, uniform routing).  While the average routed expert serves
-// few slots, the per-slot kernel wins: it needs no sort and its grid has no
-// per-workgroup setup (16 tokens, H = 2048: 48.2 vs 52.4 us; 24 tokens: 62.6
-// vs 64.3).  From two slots per expert on (B*k >= 2E) the expert-grouped
-// kernel reads each routed row once and wins (32 tokens: 70.8 vs 77.4 us at
-// H = 2048, 268 vs 300 us at H = 4096; 64 tokens: 95 vs 117 and 374 vs
-// 445 us).  Skewed routing favours it earlier (24 tokens, Zipf: 49.5 vs
-// 52.9 us), and so does H = 4096 (24 tokens: 238 vs 249 us); the threshold
-// stays at the uniform H = 2048 crossover.
-//
-// From four slots per expert on (B*k >= 4E), and from two at H >= 4096, the
-// expert-grouped product runs on the matrix cores: 64 tokens at H = 2048
-// 82.0 vs 93.0 us, at H = 4096 300 vs 360 us; 32 tokens at H = 4096 255 vs
-// 269 us, at H = 2048 71.2 vs 70.3 (the vector-unit kernel keeps that one).
-// Under Zipf routing the matrix-core kernel wins already at 32 tokens, H =
-// 2048 (55.2 vs 59.6 us); the table follows uniform routing.
+// experts, top-8; gate/up alone, uniform routing unless stated).  While the
+// average routed expert serves few slots, the per-slot kernel wins: it needs
+// no sort and its grid has no per-workgroup setup (16 tokens, H = 2048: 48.3
+// us against 49.7 on the matrix cores and 51.7 on the vector-unit grouped
+// kernel).  Once tokens share experts the expert-grouped product on the matrix
+// cores reads each routed row once and wins: at H = 2048 from 1.5 slots per
+// expert (24 tokens: 59.6 vs 62.7 us per-slot; 32 tokens: 65.6 vs 70.6
+// grouped and 77.7 per-slot), at H = 4096 from half a slot per expert (8
+// tokens: 114.0 vs 115.8; 16 tokens: 173.7 vs 188.4; 32 tokens: 233.5 vs
+// 268.8 grouped).  Skewed routing favours it earlier (16 tokens, H = 2048,
+// Zipf: 35.4 vs 38.4 us); the table follows uniform routing.  The vector-unit
+// grouped kernel is the choice from two slots per expert on where the
+// matrix-core kernel's limits exclude the shape.
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
-  if ((slots >= 4LL * E || (slots >= 2LL * E && H >= 4096)) && mfma_allowed(H, slots, E))
+  if ((2 * slots >= 3LL * E || (H >= 4096 && 2 * slots >= E)) && mfma_allowed(H, slots, E))
     return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
   if (slots >= 2LL * E && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;

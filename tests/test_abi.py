@@ -157,7 +157,7 @@ def test_conventional_path_arguments():
 
 
 def test_plans():
-    for B in (1, 8, 16, 32, 64):
+    for B in (1, 8, 16, 23, 24, 32, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
         if v == mg.MOE_GATE_UP_PER_SLOT:   # one wavefront per (tile, slot)
             assert r in (1, 2, 4, 8)
@@ -167,13 +167,16 @@ def test_plans():
             assert g == min(2048, -(-(B * 8 * -(-768 // (4 * r))) // 2))   # items taken in pairs
         else:                              # matrix cores: one resident round, two workgroups per CU
             assert v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA and r == 16 and g == 512
-        # grouped from two slots per expert on, on the matrix cores from four
-        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED) == (2 * 128 <= B * 8 < 4 * 128)
-        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (B * 8 >= 4 * 128)
-    # H = 4096: the matrix cores from two slots per expert on; H not a multiple of 2048: never
+        # on the matrix cores from 1.5 slots per expert on, per slot below
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (2 * B * 8 >= 3 * 128)
+        assert (v == mg.MOE_GATE_UP_PER_SLOT) == (2 * B * 8 < 3 * 128)
+    # H = 4096: the matrix cores from half a slot per expert on
     assert mg.moe_decode_gate_up_plan(32, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
-    assert mg.moe_decode_gate_up_plan(16, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    assert mg.moe_decode_gate_up_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
+    assert mg.moe_decode_gate_up_plan(7, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    # H not a multiple of 2048: never on the matrix cores; the vector-unit grouped kernel from two slots on
     assert mg.moe_decode_gate_up_plan(64, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED
+    assert mg.moe_decode_gate_up_plan(31, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
     for B in (1, 8, 16, 32, 64):
