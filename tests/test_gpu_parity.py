@@ -276,7 +276,7 @@ def test_single_layer_b1(dev, s1):
     _full(s1, "single_b1", 1, "uniform", dev)
 
 
-@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 24, 32])   # 24: where the table turns to the matrix cores
 def test_batch_sweep(dev, s1, B):
     _full(s1, "batch_sweep", B, "uniform", dev, variants=BOTH)
 
