@@ -9,7 +9,8 @@ may differ by one step.  Covered: small shapes (H a multiple of 2048, I from
 32 to 2048, units of 1 to 16 slots, an expert cut into several units), every E4M3 code at
 edge E8M0 scales including the shifted path for codes above 246, seeded random
 shapes with uniform or skewed routing, the S1 and S2 workloads, determinism,
-out-of-range ids and the router step in front of it.
+the kernel's limits (1024 slots over 1024 experts at H = 8192, one workgroup
+per CU), out-of-range ids and the router step in front of it.
 """
 import numpy as np
 import pytest
@@ -166,6 +167,29 @@ def test_wide_layer_sampled_tokens(dev):
         h_ref, y_ref = oracle.layer(x[toks], ids[toks], w[toks], *D.host())
         h, y = run_gpu(D, x, ids, w, dev, variant=MFMA)
         check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"mfma wide B={B} tokens={toks}")
+
+
+@pytest.mark.parametrize("shape", [(1024, 8192, 32, 1024, 1), (96, 2048, 64, 512, 8)],
+                         ids=["max: B*k=1024, E=1024, H=8192", "E=512, 1.5 slots per expert"])
+def test_large_expert_counts(dev, shape):
+    """The kernel's limits: 1024 slots over 1024 experts at H = 8192, where the
+    slot index, the chunk buffers and the scale codes take over 80 KB of LDS and
+    one workgroup runs per CU; and 768 slots over 512 experts, where the plain
+    call picks the matrix cores by itself."""
+    B, H, I, E, k = shape
+    L = mi.make_layer(400 + E, H, I, E)
+    x = mi.make_x(401, B, H)
+    ids, _ = mi.route_uniform(402, B, E, k)
+    h = torch.empty((B, k, I), dtype=torch.int16, device=dev)
+    variant = mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA if E == 1024 else 0
+    if variant == 0:
+        assert mg.moe_decode_gate_up_plan(B, H, I, E, k)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
+    mg.moe_decode_gate_up(_t(x, dev), _t(ids, dev), _t(L.w_gate, dev), _t(L.s_gate, dev), _t(L.w_up, dev),
+                          _t(L.s_up, dev), h, variant=variant)
+    torch.cuda.synchronize()
+    ref = oracle.gate_up(x, ids, L.w_gate, L.s_gate, L.w_up, L.s_up)
+    p = parity(h.cpu().numpy().view(np.uint16), ref, B * k)
+    assert passes(p), p
 
 
 def test_out_of_range_ids_give_nan(dev, s1):
