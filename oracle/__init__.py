@@ -51,8 +51,6 @@ def _bind(lib):
     lib.orc_set_threads.argtypes = [i]; lib.orc_set_threads.restype = i
     lib.orc_gate_up.argtypes = [P, P, P, P, P, P, P, P, P, P, i, i, i, i, i]; lib.orc_gate_up.restype = i
     lib.orc_down.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]; lib.orc_down.restype = i
-    lib.orc_gate_up_at.argtypes = [P, P, P, P, P, P, P, L, P, i, i, i, i, i]; lib.orc_gate_up_at.restype = i
-    lib.orc_down_at.argtypes = [P, P, P, P, P, P, L, P, i, i, i, i, i]; lib.orc_down_at.restype = i
     lib.orc_conventional.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i, i, i, i, i]; lib.orc_conventional.restype = i
     lib.orc_mx_fake_quant.argtypes = [P, L]; lib.orc_mx_fake_quant.restype = None
     lib.orc_route.argtypes = [P, P, P, i, i, i]; lib.orc_route.restype = i
@@ -162,31 +160,6 @@ def layer(x, ids, w, wg, sg, wu, su, wd, sd):
     """Both kernels: returns (h bits [B,k,I], y bits [B,H])."""
     h = gate_up(x, ids, wg, sg, wu, su)
     return h, down(h, ids, w, wd, sd)
-
-
-def gate_up_at(x, ids, wg, sg, wu, su, items):
-    """h at the given (b, j, n) triples (int64 [n,3])."""
-    x = _c(x, np.uint16); ids = _c(ids, np.int32)
-    wg = _c(wg, np.uint8); sg = _c(sg, np.uint8); wu = _c(wu, np.uint8); su = _c(su, np.uint8)
-    items = _c(items, np.int64).reshape(-1, 3)
-    B, H = x.shape
-    k = ids.shape[1]
-    E, I, _ = wg.shape
-    out = np.empty(len(items), np.uint16)
-    _check(load().orc_gate_up_at(_p(x), _p(ids), _p(wg), _p(sg), _p(wu), _p(su), _p(items), len(items), _p(out), B, H, I, E, k))
-    return out
-
-
-def down_at(h, ids, w, wd, sd, items):
-    """y at the given (b, o) pairs (int64 [n,2]), from the given h bits [B,k,I]."""
-    h = _c(h, np.uint16); ids = _c(ids, np.int32); w = _c(w, np.float32)
-    wd = _c(wd, np.uint8); sd = _c(sd, np.uint8)
-    items = _c(items, np.int64).reshape(-1, 2)
-    B, k, I = h.shape
-    E, H, _ = wd.shape
-    out = np.empty(len(items), np.uint16)
-    _check(load().orc_down_at(_p(h), _p(ids), _p(w), _p(wd), _p(sd), _p(items), len(items), _p(out), B, H, I, E, k))
-    return out
 
 
 def conventional(x, ids, w, wg, sg, wu, su, wd, sd, *, fp64=False):

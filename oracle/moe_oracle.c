@@ -253,59 +253,6 @@ int orc_down(const uint16_t *h, const int32_t *ids, const float *tw,
 }
 
 /* ------------------------------------------------------------------ */
-/* Sampled outputs (for full-size checks)                              */
-/* ------------------------------------------------------------------ */
-
-/* items: n triples (b, j, n); h_out[i] = h at that triple. */
-int orc_gate_up_at(const uint16_t *x, const int32_t *ids,
-                   const uint8_t *wg, const uint8_t *sg, const uint8_t *wu, const uint8_t *su,
-                   const int64_t *items, long n_items, uint16_t *h_out,
-                   int B, int H, int I, int E, int k)
-{
-    long t;
-    int rc;
-    if (!x || !ids || !wg || !sg || !wu || !su || !items || !h_out)
-        return -1;
-    if ((rc = check_shape(B, H, I, E, k)) || (rc = check_ids(ids, B, E, k)))
-        return rc;
-    for (t = 0; t < n_items; ++t) {
-        long b = items[3 * t], j = items[3 * t + 1], n = items[3 * t + 2];
-        if (b < 0 || b >= B || j < 0 || j >= k || n < 0 || n >= I)
-            return -2;
-    }
-#pragma omp parallel for schedule(dynamic, 16)
-    for (t = 0; t < n_items; ++t) {
-        double G, U;
-        gate_up_one(x, ids, wg, sg, wu, su, H, I, k, items[3 * t], items[3 * t + 1], items[3 * t + 2], &G, &U);
-        h_out[t] = orc_bf16_rne(orc_silu(G) * U);
-    }
-    return 0;
-}
-
-/* items: n pairs (b, o); y_out[i] = y at that pair, from the given h. */
-int orc_down_at(const uint16_t *h, const int32_t *ids, const float *tw,
-                const uint8_t *wd, const uint8_t *sd,
-                const int64_t *items, long n_items, uint16_t *y_out,
-                int B, int H, int I, int E, int k)
-{
-    long t;
-    int rc;
-    if (!h || !ids || !tw || !wd || !sd || !items || !y_out)
-        return -1;
-    if ((rc = check_shape(B, H, I, E, k)) || (rc = check_ids(ids, B, E, k)))
-        return rc;
-    for (t = 0; t < n_items; ++t) {
-        long b = items[2 * t], o = items[2 * t + 1];
-        if (b < 0 || b >= B || o < 0 || o >= H)
-            return -2;
-    }
-#pragma omp parallel for schedule(dynamic, 16)
-    for (t = 0; t < n_items; ++t)
-        y_out[t] = orc_bf16_rne(down_one(h, ids, tw, wd, sd, H, I, k, items[2 * t], items[2 * t + 1]));
-    return 0;
-}
-
-/* ------------------------------------------------------------------ */
 /* Conventional expert-centric path, numerically emulated               */
 /* ------------------------------------------------------------------ */
 
