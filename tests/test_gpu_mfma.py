@@ -20,7 +20,7 @@ import moe_gate_up_amd as mg
 import moe_inputs as mi
 import oracle
 from oracle.compare import parity, passes
-from tests.test_gpu_parity import DevLayer, _t, check, run_gpu
+from tests.test_gpu_parity import DevLayer, _t, check, run_gpu, wide_case
 
 pytestmark = pytest.mark.gpu
 
@@ -156,17 +156,12 @@ def test_s1_workload(dev, s1, B, routing):
     assert np.array_equal(h, h2) and np.array_equal(y, y2)
 
 
-def test_wide_layer_sampled_tokens(dev):
-    s = mi.SHAPES["S2"]
-    D = DevLayer(mi.make_layer(mi.layer_seed("wide_layers", 0), s["H"], s["I"], s["E"]), dev)
-    for B in (32, 64):
-        seed = mi.routing_seed("wide_layers", B, layer=0)
-        x = mi.make_x(seed, B, D.H)
-        ids, w = mi.route_uniform(seed, B, D.E, 8)
-        toks = sorted({0, B // 3, B - 1})
-        h_ref, y_ref = oracle.layer(x[toks], ids[toks], w[toks], *D.host())
-        h, y = run_gpu(D, x, ids, w, dev, variant=MFMA)
-        check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"mfma wide B={B} tokens={toks}")
+@pytest.mark.parametrize("B", [16, 32, 64])
+def test_wide_layer(dev, s2, B):
+    """Every token of the wide workload's batch (H=4096, I=1536)."""
+    x, ids, w, h_ref, y_ref = wide_case(s2, B)
+    h, y = run_gpu(s2, x, ids, w, dev, variant=MFMA)
+    check(h, y, h_ref, y_ref, B, 8, f"mfma wide B={B}")
 
 
 @pytest.mark.parametrize("shape", [(1024, 8192, 32, 1024, 1), (96, 2048, 64, 512, 8)],
@@ -225,3 +220,49 @@ def test_routed(dev, s1):
     h_ref = oracle.gate_up(x, ri, s1.L.w_gate, s1.L.s_gate, s1.L.w_up, s1.L.s_up)
     p = parity(h.cpu().numpy().view(np.uint16), h_ref, B * 8)
     assert passes(p), p
+
+
+def test_two_host_threads_two_streams(dev, s1):
+    """Calls from two host threads on two streams, with shapes whose LDS needs
+    differ (64 tokens over 128 experts; 4 tokens over 8 experts at I = 96), each
+    thread launching 40 times before it synchronises: both results match the
+    oracle (the library keeps no per-call state that one call could change under
+    another)."""
+    import threading
+
+    small = DevLayer(mi.make_layer(500, 2048, 96, 8), dev)
+    cases = []
+    for D, B, E, seed in ((s1, 64, s1.E, 501), (small, 4, 8, 502)):
+        x = mi.make_x(seed, B, D.H)
+        ids, w = mi.route_uniform(seed, B, E, 8 if E > 8 else 4)
+        cases.append((D, x, ids, w))
+    out = [None, None]
+    errs = []
+
+    def work(i):
+        try:
+            D, x, ids, w = cases[i]
+            B, k = ids.shape
+            st = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(st):
+                xd, idd = _t(x, dev), _t(ids, dev)
+                h = torch.empty((B, k, D.I), dtype=torch.int16, device=dev)
+                st.synchronize()
+                for _ in range(40):
+                    mg.moe_decode_gate_up(xd, idd, D.wg, D.sg, D.wu, D.su, h, stream=st,
+                                          variant=mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA)
+                st.synchronize()
+                out[i] = h.cpu().numpy().view(np.uint16)
+        except Exception as e:   # reported by the main thread
+            errs.append(e)
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs, errs
+    for (D, x, ids, w), h in zip(cases, out):
+        ref = oracle.gate_up(x, ids, D.L.w_gate, D.L.s_gate, D.L.w_up, D.L.s_up)
+        p = parity(h, ref, ids.size)
+        assert passes(p), p

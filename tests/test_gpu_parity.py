@@ -6,9 +6,9 @@ GPU accumulates in FP32, so a few elements may differ by one bf16 step.
 Covered: every E4M3 code and E8M0 edge scale through the real kernel, small
 shapes spanning several tiles with ragged tails and every rows-per-wave
 variant, 24 seeded random shapes (ragged H, I, E, k, B; both kernel families;
-uniform or skewed routing), the five synthetic workloads at full size (the 48- and 8-layer
-workloads on a subset of their layers, the B=64 wide shape on sampled
-tokens), empty batches, out-of-range expert ids, full coverage of the outputs
+uniform or skewed routing), the five synthetic workloads at full size and
+every token of their batches (the 48-layer workload on layers 1, 24 and 47,
+the 8-layer wide workload on layer 0), empty batches, out-of-range expert ids, full coverage of the outputs
 (sentinels and guard words), determinism and non-default streams.
 """
 import numpy as np
@@ -68,6 +68,10 @@ def run_gpu(D, x, ids, w, dev, rows_gu=None, rows_dn=None, stream=None, variant=
     return h.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16)
 
 
+# at most one element in N_DIFF_DIV may differ from the oracle's bf16 at all
+N_DIFF_DIV = 200
+
+
 def check(h, y, h_ref, y_ref, B, k, what=""):
     ph = parity(h, h_ref, B * k)
     py = parity(y, y_ref, B)
@@ -75,8 +79,10 @@ def check(h, y, h_ref, y_ref, B, k, what=""):
     assert passes(ph), (what, ph)
     assert passes(py), (what, py)
     # FP32 accumulation flips the bf16 rounding of a few near-ties (and y inherits h's
-    # flips); a systematic rounding error (e.g. truncation) would flip about half
-    assert ph["n_diff"] <= max(8, ph["n"] // 20) and py["n_diff"] <= max(8, py["n"] // 20)
+    # flips): at most a few per ten thousand elements in every recorded run.  A
+    # systematic rounding error (e.g. truncation) would flip about half.
+    assert ph["n_diff"] <= max(8, ph["n"] // N_DIFF_DIV) and py["n_diff"] <= max(8, py["n"] // N_DIFF_DIV)
+    return ph, py
 
 
 # --------------------------------------------------------------- decode path
@@ -286,7 +292,7 @@ def test_routing_stress_b32(dev, s1, routing):
     _full(s1, "routing_stress", 32, routing, dev, variants=BOTH)
 
 
-@pytest.mark.parametrize("layer", [1, 47])
+@pytest.mark.parametrize("layer", [1, 24, 47])
 def test_decode_step_layers(dev, layer):
     s = mi.SHAPES["S1"]
     D = DevLayer(mi.make_layer(mi.layer_seed("decode_step", layer), s["H"], s["I"], s["E"]), dev)
@@ -299,18 +305,27 @@ def test_decode_step_layers(dev, layer):
         check(h, y, h_ref, y_ref, B, 8, f"decode step layer={layer} B={B}")
 
 
-def test_wide_layer_sampled_tokens(dev):
-    s = mi.SHAPES["S2"]
-    D = DevLayer(mi.make_layer(mi.layer_seed("wide_layers", 0), s["H"], s["I"], s["E"]), dev)
-    for B in (1, 16, 32, 64):
+_WIDE_REF = {}
+
+
+def wide_case(D, B):
+    """Inputs and the oracle's h, y for the whole batch of B tokens of the wide
+    workload's layer 0 (computed once per process)."""
+    if B not in _WIDE_REF:
         seed = mi.routing_seed("wide_layers", B, layer=0)
         x = mi.make_x(seed, B, D.H)
         ids, w = mi.route_uniform(seed, B, D.E, 8)
-        toks = sorted({0, B // 2, B - 1})
-        h_ref, y_ref = oracle.layer(x[toks], ids[toks], w[toks], *D.host())
-        for v in BOTH:
-            h, y = run_gpu(D, x, ids, w, dev, variant=v)
-            check(h[toks], y[toks], h_ref, y_ref, len(toks), 8, f"wide layer B={B} tokens={toks} variant={v}")
+        _WIDE_REF[B] = (x, ids, w) + tuple(oracle.layer(x, ids, w, *D.host()))
+    return _WIDE_REF[B]
+
+
+@pytest.mark.parametrize("B", [1, 16, 32, 64])
+def test_wide_layer(dev, s2, B):
+    """Every token of the batch, every kernel family."""
+    x, ids, w, h_ref, y_ref = wide_case(s2, B)
+    for v in BOTH:
+        h, y = run_gpu(s2, x, ids, w, dev, variant=v)
+        check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} variant={v}")
 
 
 # --------------------------------------------------------------- properties
