@@ -42,7 +42,10 @@
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *     null stream).  The call returns as soon as the launch is enqueued; the
  *     caller synchronises the stream before reading outputs.
- *   - Calls are thread-safe (the library has no mutable state).
+ *   - Calls are thread-safe.  The only state the library keeps is set once
+ *     per device, before the first launch of the matrix-core kernel on that
+ *     device, and is never changed afterwards: that kernel's maximum dynamic
+ *     LDS, set to the largest size its limits allow.
  *   - Outputs are fully overwritten; every element is written exactly once.
  *   - Outputs must not overlap any input (checked on the host).
  *   - B == 0 is a valid no-op.

@@ -3,6 +3,7 @@
 // stated in include/moe_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <utility>
 
 #include "moe_decode.h"
@@ -259,6 +260,32 @@ bool mfma_allowed(int H, long long slots, int E) {
   return H % 2048 == 0 && H <= 8192 && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts;
 }
 
+// Largest dynamic LDS the matrix-core kernel takes within its limits (1024
+// slots over 1024 experts at H = 8192: ~92 KB).  The kernel's attribute is set
+// to it once per device, before the first launch on that device, and never
+// changed afterwards: a per-call value would be process-wide state that a
+// concurrent call could lower between another thread's set and its launch.
+// Occupancy follows the LDS size each launch asks for, not this maximum.
+constexpr int kMfmaMaxLds = moe::mfma_lds_bytes(moe::kSortMaxExperts, moe::kSortMaxSlots, 8192);
+static_assert(kMfmaMaxLds <= kLdsPerCu, "the matrix-core kernel's largest LDS must fit one CU");
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_mfma_attr_once[kMaxDevices];
+hipError_t g_mfma_attr_rc[kMaxDevices];
+
+// hipSuccess once the attribute is in place on the current device.
+hipError_t mfma_setup_current_device() {
+  int dev = 0;
+  hipError_t rc = hipGetDevice(&dev);
+  if (rc != hipSuccess) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_mfma_attr_once[dev], [dev] {
+    g_mfma_attr_rc[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_gate_up_grouped_mfma_w64),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaMaxLds);
+  });
+  return g_mfma_attr_rc[dev];
+}
+
 long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
                       const uint8_t* sg, const uint8_t* wu, const uint8_t* su, void* h, int B, int H, int I, int E,
                       int k, const RouteIO* ro) {
@@ -272,8 +299,6 @@ long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids
     launch_route(st, *ro, B, E, k);
     ids = ro->ids;
   }
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_gate_up_grouped_mfma_w64),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   hipLaunchKernelGGL(moe::moe_gate_up_grouped_mfma_w64, dim3((unsigned)blocks), dim3(256), (unsigned)lds, st,
                      static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k);
   return blocks;
@@ -397,6 +422,7 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
   }
   const long long blocks = fn(false, nullptr, x, ids, wg, sg, wu, su, h, B, H, I, E, k, ro);
   if (blocks * kWavesPerBlock >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (variant == MOE_GATE_UP_EXPERT_GROUPED_MFMA && mfma_setup_current_device() != hipSuccess) return MOE_ERR_LAUNCH;
   (void)hipGetLastError();
   fn(true, static_cast<hipStream_t>(stream), x, ids, wg, sg, wu, su, h, B, H, I, E, k, ro);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
