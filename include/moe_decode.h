@@ -76,6 +76,8 @@ extern "C" {
 #define MOE_ERR_LAUNCH (-4)      /* the HIP runtime reported an error for the launch          */
 #define MOE_ERR_ALIAS (-5)       /* an output range overlaps an input range                   */
 #define MOE_ERR_ARG (-6)         /* an invalid tuning argument (see the _ex variants)         */
+#define MOE_ERR_SCRATCH (-7)     /* the shape needs more scratch than the fixed buffer holds  */
+                                 /* (moe_decode_conventional_noalloc only)                   */
 
 /* Gate/up kernel: h[b,j,n] = bf16( SiLU(G) * U ), with
  *   G = sum_c dec(w_gate[e,n,c]) * 2^(s_gate[e,n,c/32]-127) * x[b,c],
@@ -233,6 +235,27 @@ int moe_decode_conventional(const void *x, const int32_t *topk_ids, const float 
                             const uint8_t *w_down, const uint8_t *s_down,
                             void *y_out, void *workspace, size_t workspace_bytes,
                             int B, int H, int I, int E, int k, void *stream);
+
+/* The conventional path of moe_decode_conventional for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Same stages, kernels and results, but
+ * instead of a caller's workspace the launches use a fixed 32 MiB device
+ * buffer inside the library (one per device, resident from module load until
+ * the process ends).  Nothing in that buffer needs to start at zero: the route
+ * stage writes every entry the later stages read.  The call allocates and
+ * frees nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's address of the buffer once.
+ * Every call on one device shares that device's buffer and leaves its contents
+ * behind, so calls that overlap in time on one device race: the caller orders
+ * them (one stream, or events between streams).  Returns MOE_ERR_SCRATCH
+ * (before any launch) when the shape's workspace,
+ * moe_decode_conventional_workspace(), exceeds 32 MiB; otherwise the codes
+ * and limits of moe_decode_conventional. */
+int moe_decode_conventional_noalloc(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                                    const uint8_t *w_gate, const uint8_t *s_gate,
+                                    const uint8_t *w_up, const uint8_t *s_up,
+                                    const uint8_t *w_down, const uint8_t *s_down,
+                                    void *y_out, int B, int H, int I, int E, int k, void *stream);
 
 /* Bandwidth probes that set the denominator of the efficiency figure (blog
  * post, "Hardware efficiency": peak measured with a copy kernel over

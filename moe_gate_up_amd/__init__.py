@@ -25,6 +25,7 @@ MOE_ERR_ALIGN = -3
 MOE_ERR_LAUNCH = -4
 MOE_ERR_ALIAS = -5
 MOE_ERR_ARG = -6
+MOE_ERR_SCRATCH = -7
 MOE_GATE_UP_PER_SLOT = 1
 MOE_GATE_UP_EXPERT_GROUPED = 2
 MOE_GATE_UP_EXPERT_GROUPED_MFMA = 3
@@ -34,7 +35,7 @@ MOE_DOWN_EXPERT_GROUPED = 2
 EXPORTS = (
     "moe_decode_gate_up", "moe_decode_down", "moe_decode_gate_up_ex", "moe_decode_down_ex",
     "moe_decode_gate_up_plan", "moe_decode_down_plan", "moe_decode_conventional_workspace",
-    "moe_decode_conventional", "moe_decode_route", "moe_decode_gate_up_routed", "moe_decode_gate_up_routed_ex",
+    "moe_decode_conventional", "moe_decode_conventional_noalloc", "moe_decode_route", "moe_decode_gate_up_routed", "moe_decode_gate_up_routed_ex",
     "moe_decode_copy_peak", "moe_decode_read_peak",
     "moe_decode_strerror",
 )
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
             L.moe_decode_down_plan.argtypes = [I] * 5 + [IP, IP, IP]
             L.moe_decode_conventional_workspace.argtypes = [I] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
             L.moe_decode_conventional.argtypes = [P] * 11 + [S] + [I] * 5 + [P]
+            L.moe_decode_conventional_noalloc.argtypes = [P] * 10 + [I] * 5 + [P]
             L.moe_decode_route.argtypes = [P] * 3 + [I] * 3 + [P]
             L.moe_decode_gate_up_routed.argtypes = [P] * 9 + [I] * 5 + [P]
             L.moe_decode_gate_up_routed_ex.argtypes = [P] * 9 + [I] * 7 + [P]
@@ -248,6 +250,29 @@ def moe_decode_conventional(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_u
     rc = lib().moe_decode_conventional(*args, _stream(stream))
     if rc:
         raise MoeDecodeError(rc, "moe_decode_conventional")
+    return y_out
+
+
+def moe_decode_conventional_noalloc(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y_out,
+                                    stream=None):
+    """The expert-centric path on the library's fixed scratch buffer, with no
+    workspace and no allocation (see include/moe_decode.h)."""
+    T = _types()
+    B, H = x.shape
+    k = topk_ids.shape[-1]
+    E, I = w_gate.shape[0], w_gate.shape[1]
+    wb = E * I * H
+    args = [
+        _dev(x, "x", B * H, T["bf16"]), _dev(topk_ids, "topk_ids", B * k, T["i32"]),
+        _dev(topk_weights, "topk_weights", B * k, T["f32"]),
+        _dev(w_gate, "w_gate", wb, T["u8"]), _dev(s_gate, "s_gate", wb // 32, T["u8"]),
+        _dev(w_up, "w_up", wb, T["u8"]), _dev(s_up, "s_up", wb // 32, T["u8"]),
+        _dev(w_down, "w_down", wb, T["u8"]), _dev(s_down, "s_down", wb // 32, T["u8"]),
+        _dev(y_out, "y_out", B * H, T["bf16"]), B, H, I, E, k,
+    ]
+    rc = lib().moe_decode_conventional_noalloc(*args, _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_conventional_noalloc")
     return y_out
 
 

@@ -618,27 +618,43 @@ ConvGemv pick_conv_np(int np, std::integer_sequence<int, NPs...>) {
   return fn;
 }
 
-int conventional_impl(const void* x, const int32_t* ids, const float* tw, const uint8_t* wg, const uint8_t* sg,
-                      const uint8_t* wu, const uint8_t* su, const uint8_t* wd, const uint8_t* sd, void* y, void* ws,
-                      size_t ws_bytes, int B, int H, int I, int E, int k, void* stream) {
+// Every check of the conventional path's arguments except the workspace's.
+int conventional_check(const void* x, const int32_t* ids, const float* tw, const uint8_t* wg, const uint8_t* sg,
+                       const uint8_t* wu, const uint8_t* su, const uint8_t* wd, const uint8_t* sd, const void* y,
+                       int B, int H, int I, int E, int k) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
   if ((long long)B * k > moe::kConvMaxSlots || E > moe::kConvMaxSlots || passes(H) > kConvMaxPasses ||
       passes(I) > kConvMaxPasses)
     return MOE_ERR_SHAPE;
   if (B == 0) return MOE_OK;
-  if (!x || !ids || !tw || !wg || !sg || !wu || !su || !wd || !sd || !y || !ws) return MOE_ERR_NULL;
+  if (!x || !ids || !tw || !wg || !sg || !wu || !su || !wd || !sd || !y) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(y, 2) ||
-      !aligned(ids, 4) || !aligned(tw, 4) || !aligned(ws, 256))
+      !aligned(ids, 4) || !aligned(tw, 4))
     return MOE_ERR_ALIGN;
-  const ConvLayout L(B, H, I, E, k);
-  if (ws_bytes < L.total) return MOE_ERR_ARG;
   const size_t yb = (size_t)B * H * 2, wb = (size_t)E * I * H;
   const void* ins[] = {x, ids, tw, wg, sg, wu, su, wd, sd};
   const size_t insz[] = {(size_t)B * H * 2, (size_t)B * k * 4, (size_t)B * k * 4, wb, wb / 32, wb, wb / 32, wb, wb / 32};
   for (int i = 0; i < 9; ++i)
-    if (overlaps(y, yb, ins[i], insz[i]) || overlaps(ws, L.total, ins[i], insz[i])) return MOE_ERR_ALIAS;
-  if (overlaps(y, yb, ws, L.total)) return MOE_ERR_ALIAS;
+    if (overlaps(y, yb, ins[i], insz[i])) return MOE_ERR_ALIAS;
+  return MOE_OK;
+}
+
+int conventional_impl(const void* x, const int32_t* ids, const float* tw, const uint8_t* wg, const uint8_t* sg,
+                      const uint8_t* wu, const uint8_t* su, const uint8_t* wd, const uint8_t* sd, void* y, void* ws,
+                      size_t ws_bytes, int B, int H, int I, int E, int k, void* stream) {
+  int rc = conventional_check(x, ids, tw, wg, sg, wu, su, wd, sd, y, B, H, I, E, k);
+  if (rc || B == 0) return rc;
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
+  const ConvLayout L(B, H, I, E, k);
+  if (ws_bytes < L.total) return MOE_ERR_ARG;
+  const size_t wb = (size_t)E * I * H;
+  const void* ins[] = {x, ids, tw, wg, sg, wu, su, wd, sd, y};
+  const size_t insz[] = {(size_t)B * H * 2, (size_t)B * k * 4, (size_t)B * k * 4, wb, wb / 32, wb, wb / 32, wb, wb / 32,
+                         (size_t)B * H * 2};
+  for (int i = 0; i < 10; ++i)
+    if (overlaps(ws, L.total, ins[i], insz[i])) return MOE_ERR_ALIAS;
   ConvGemv gu = pick_conv_np<true>(passes(H), std::make_integer_sequence<int, kConvMaxPasses>{});
   ConvGemv dn = pick_conv_np<false>(passes(I), std::make_integer_sequence<int, kConvMaxPasses>{});
   if (!gu || !dn) return MOE_ERR_SHAPE;
@@ -669,6 +685,34 @@ int conventional_impl(const void* x, const int32_t* ids, const float* tw, const 
   hipLaunchKernelGGL(moe::conv_combine_kernel, blocks((long long)B * H), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t*>(w8 + L.ob), slot_row, tw, static_cast<uint16_t*>(y), B, H, k);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------- conventional path, no allocation
+// A fixed device buffer for callers that cannot allocate (code under graph
+// capture, serving loops, harnesses that forbid hipMalloc): it stands in for
+// the caller's workspace.  32 MiB holds the workspace of every decode shape
+// measured here (H=2048, I=768, 128 experts, top-8 up to 128 tokens: 17 MB;
+// H=4096, I=1536 up to 64 tokens: 17 MB).  Each device holds its own copy from
+// module load until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kConvScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kConvScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr on failure).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_rc[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_rc[dev] == hipSuccess ? p : nullptr;
+  });
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -745,6 +789,21 @@ int moe_decode_conventional(const void* x, const int32_t* topk_ids, const float*
                            workspace_bytes, B, H, I, E, k, stream);
 }
 
+int moe_decode_conventional_noalloc(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                                    const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                                    const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down, void* y_out,
+                                    int B, int H, int I, int E, int k, void* stream) {
+  // Every check that needs no device comes first; then the fixed buffer's size.
+  int rc = conventional_check(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y_out, B, H, I,
+                              E, k);
+  if (rc || B == 0) return rc;
+  if (ConvLayout(B, H, I, E, k).total > kConvScratchBytes) return MOE_ERR_SCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_LAUNCH;
+  return conventional_impl(x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y_out, ws,
+                           kConvScratchBytes, B, H, I, E, k, stream);
+}
+
 int moe_decode_gate_up_plan(int B, int H, int I, int E, int k, int* variant, int* rows_per_wave, int* workgroups) {
   int rc = check_shape(B, H, I, E, k);
   if (rc) return rc;
@@ -808,6 +867,7 @@ const char* moe_decode_strerror(int code) {
     case MOE_ERR_LAUNCH: return "the HIP runtime reported a launch error";
     case MOE_ERR_ALIAS: return "an output overlaps an input";
     case MOE_ERR_ARG: return "invalid tuning argument";
+    case MOE_ERR_SCRATCH: return "the shape needs more scratch memory than the library's fixed buffer holds (32 MiB)";
   }
   return "unknown error code";
 }

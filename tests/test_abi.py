@@ -156,6 +156,29 @@ def test_conventional_path_arguments():
     assert cv(ws=A + 3 * S + 4096) == mg.MOE_ERR_ALIAS         # workspace overlapping the gate weights
 
 
+def cvn(x=A, ids=A + 1 * S, tw=A + 2 * S, wg=A + 3 * S, sg=A + 4 * S, wu=A + 5 * S, su=A + 6 * S, wd=A + 7 * S,
+        sd=A + 8 * S, y=A + 9 * S, B=2, H=2048, I=768, E=128, k=8):
+    L = mg.lib()
+    args = [ctypes.c_void_p(p) for p in (x, ids, tw, wg, sg, wu, su, wd, sd, y)]
+    return L.moe_decode_conventional_noalloc(*args, B, H, I, E, k, None)
+
+
+def test_conventional_noalloc_arguments():
+    """The no-allocation form checks the same arguments before touching the
+    device, and refuses shapes whose workspace exceeds its 32 MiB buffer."""
+    assert cvn(B=0) == mg.MOE_OK
+    assert cvn(x=0) == mg.MOE_ERR_NULL
+    assert cvn(x=A + 8) == mg.MOE_ERR_ALIGN
+    assert cvn(B=129) == mg.MOE_ERR_SHAPE                      # B*k > 1024
+    assert cvn(y=A + 64) == mg.MOE_ERR_ALIAS                   # y overlapping x
+    # 17 MB at 128 tokens of the H=2048 layer and at 64 tokens of the H=4096 one: accepted sizes
+    assert mg.moe_decode_conventional_workspace(128, 2048, 768, 128, 8) <= 32 << 20
+    assert mg.moe_decode_conventional_workspace(64, 4096, 1536, 128, 8) <= 32 << 20
+    need = mg.moe_decode_conventional_workspace(128, 8192, 1536, 128, 8)
+    assert need > 32 << 20
+    assert cvn(B=128, H=8192, I=1536) == mg.MOE_ERR_SCRATCH
+
+
 def test_plans():
     for B in (1, 8, 16, 23, 24, 32, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
