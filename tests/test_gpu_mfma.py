@@ -59,7 +59,7 @@ def test_small_shapes(dev, shape):
     ids, w = mi.route_uniform(31 + B, B, E, k)
     h, y = run_gpu(D, x, ids, w, dev, variant=MFMA)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
-    check(h, y, h_ref, y_ref, B, k, f"mfma {shape}")
+    check(h, y, h_ref, y_ref, B, k, f"mfma {shape}", own=(D, ids, w))
 
 
 @pytest.mark.parametrize("scale", [127, 120, 134, 1, 0, 246, 247, 253, 254, 255])
@@ -134,7 +134,8 @@ def test_random_shapes(dev, i):
     ids, w = (mi.route_zipf if skew else mi.route_uniform)(9800 + i, B, E, k)
     h, y = run_gpu(D, x, ids, w, dev, variant=MFMA)
     h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
-    check(h, y, h_ref, y_ref, B, k, f"mfma random {i}: B={B} H={H} I={I} E={E} k={k} skew={skew}")
+    check(h, y, h_ref, y_ref, B, k, f"mfma random {i}: B={B} H={H} I={I} E={E} k={k} skew={skew}",
+          own=(D, ids, w))
 
 
 @pytest.fixture(scope="module")
@@ -151,7 +152,7 @@ def test_s1_workload(dev, s1, B, routing):
     ids, w = mi.make_routing(routing, seed, B, s1.E, 8)
     h, y = run_gpu(s1, x, ids, w, dev, variant=MFMA)
     h_ref, y_ref = oracle.layer(x, ids, w, *s1.host())
-    check(h, y, h_ref, y_ref, B, 8, f"mfma S1 B={B} {routing}")
+    check(h, y, h_ref, y_ref, B, 8, f"mfma S1 B={B} {routing}", own=(s1, ids, w))
     h2, y2 = run_gpu(s1, x, ids, w, dev, variant=MFMA)
     assert np.array_equal(h, h2) and np.array_equal(y, y2)
 
@@ -161,7 +162,7 @@ def test_wide_layer(dev, s2, B):
     """Every token of the wide workload's batch (H=4096, I=1536)."""
     x, ids, w, h_ref, y_ref = wide_case(s2, B)
     h, y = run_gpu(s2, x, ids, w, dev, variant=MFMA)
-    check(h, y, h_ref, y_ref, B, 8, f"mfma wide B={B}")
+    check(h, y, h_ref, y_ref, B, 8, f"mfma wide B={B}", own=(s2, ids, w))
 
 
 @pytest.mark.parametrize("shape", [(1024, 8192, 32, 1024, 1), (96, 2048, 64, 512, 8)],

@@ -35,7 +35,7 @@ def _row(workload, B, routing, D, x, ids, w, dev, h_ref=None, y_ref=None):
     if h_ref is None:
         h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
     h, y = run_gpu(D, x, ids, w, dev)
-    ph, py = check(h, y, h_ref, y_ref, B, ids.shape[1], f"report {workload} B={B} {routing}")
+    ph, py = check(h, y, h_ref, y_ref, B, ids.shape[1], f"report {workload} B={B} {routing}", own=(D, ids, w))
     vg, _, _ = mg.moe_decode_gate_up_plan(B, D.H, D.I, D.E, ids.shape[1])
     vd, _, _ = mg.moe_decode_down_plan(B, D.H, D.I, D.E, ids.shape[1])
     r = {"workload": workload, "B": B, "routing": routing, "gate_up_variant": vg, "down_variant": vd}

@@ -111,7 +111,7 @@ def check_routed(D, x, logits, k, got, what):
     Lh = D.L
     h_ref = oracle.gate_up(x, ri, Lh.w_gate, Lh.s_gate, Lh.w_up, Lh.s_up)
     y_ref = oracle.down(h_ref, ri, rw.astype(np.float32), Lh.w_down, Lh.s_down)
-    check(h, y, h_ref, y_ref, x.shape[0], k, what)
+    check(h, y, h_ref, y_ref, x.shape[0], k, what, own=(D, ids, w))
 
 
 ROUTED_SMALL = [
