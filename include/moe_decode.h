@@ -138,10 +138,20 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     every token's k contributions in slot order and writes y once.  No
  *     per-expert output buffer, no combine.  Same outputs; requires
  *     B <= 64, B*k <= 1024, E <= 1024 and I <= 2048.
+ *   MOE_DOWN_EXPERT_GROUPED_MFMA: the same organisation (one workgroup per 8
+ *     output dimensions for every token, work units of at most 8 slots of one
+ *     expert, contributions added in slot order) with the dot products on the
+ *     matrix cores (v_mfma_f32_4x4x4_16b_bf16): a wavefront converts its
+ *     unit's 8 rows to bf16 once per 4 slots and forms the 8 x 4 dot products
+ *     as 16-element chunk products, each scaled by its chunk's E8M0 scale
+ *     (exact) before the chunks are summed.  Same outputs within the same
+ *     tolerance; requires B*k <= 1024, E <= 1024 and I <= 2048
+ *     (rows_per_wave must be 0 or 8).
  * The plain call takes the grouped variant once B*k >= E (an average of one
  * or more slots per expert) and the limits allow it, else the per-token one. */
 #define MOE_DOWN_PER_TOKEN 1
 #define MOE_DOWN_EXPERT_GROUPED 2
+#define MOE_DOWN_EXPERT_GROUPED_MFMA 3
 
 /* Tuning variants of the two calls: the same contract and results within the
  * same tolerance, with the launch shape given explicitly instead of taken

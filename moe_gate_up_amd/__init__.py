@@ -31,6 +31,7 @@ MOE_GATE_UP_EXPERT_GROUPED = 2
 MOE_GATE_UP_EXPERT_GROUPED_MFMA = 3
 MOE_DOWN_PER_TOKEN = 1
 MOE_DOWN_EXPERT_GROUPED = 2
+MOE_DOWN_EXPERT_GROUPED_MFMA = 3
 
 EXPORTS = (
     "moe_decode_gate_up", "moe_decode_down", "moe_decode_gate_up_ex", "moe_decode_down_ex",

@@ -9,6 +9,7 @@
 #include "moe_decode.h"
 #include "down.hpp"
 #include "down_grouped.hpp"
+#include "down_grouped_mfma.hpp"
 #include "conventional.hpp"
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
@@ -270,20 +271,31 @@ constexpr int kMfmaMaxLds = moe::mfma_lds_bytes(moe::kSortMaxExperts, moe::kSort
 static_assert(kMfmaMaxLds <= kLdsPerCu, "the matrix-core kernel's largest LDS must fit one CU");
 
 constexpr int kMaxDevices = 64;
-std::once_flag g_mfma_attr_once[kMaxDevices];
-hipError_t g_mfma_attr_rc[kMaxDevices];
+
+// Runs f() once per device, on the first call made with that device current,
+// and returns its result on every call.
+struct PerDeviceOnce {
+  std::once_flag flag[kMaxDevices];
+  hipError_t rc[kMaxDevices];
+  template <class F>
+  hipError_t operator()(F f) {
+    int dev = 0;
+    hipError_t r = hipGetDevice(&dev);
+    if (r != hipSuccess) return r;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(flag[dev], [&] { rc[dev] = f(); });
+    return rc[dev];
+  }
+};
+
+PerDeviceOnce g_gate_up_mfma_setup;
 
 // hipSuccess once the attribute is in place on the current device.
 hipError_t mfma_setup_current_device() {
-  int dev = 0;
-  hipError_t rc = hipGetDevice(&dev);
-  if (rc != hipSuccess) return rc;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::call_once(g_mfma_attr_once[dev], [dev] {
-    g_mfma_attr_rc[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_gate_up_grouped_mfma_w64),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaMaxLds);
+  return g_gate_up_mfma_setup([] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_gate_up_grouped_mfma_w64),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaMaxLds);
   });
-  return g_mfma_attr_rc[dev];
 }
 
 long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids, const uint8_t* wg,
@@ -522,6 +534,63 @@ DownLaunch pick_down_grouped(int np) {
   return nullptr;
 }
 
+// ---------------------------------------------------------------- down, expert-grouped on the matrix cores
+// One workgroup per 8 output dimensions; rounds of 256 elements over I (I <= 2048).
+bool down_mfma_allowed(int I, long long slots, int E) {
+  return (I + 255) / 256 <= moe::kDownMfmaMaxRounds && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts;
+}
+
+// Largest dynamic LDS of the matrix-core down kernel with NR rounds.
+template <int NR>
+constexpr int down_mfma_max_lds() { return moe::down_mfma_lds_bytes(NR, moe::kSortMaxExperts, moe::kSortMaxSlots); }
+template <int... NRs>
+constexpr bool down_mfma_lds_fits(std::integer_sequence<int, NRs...>) {
+  return ((down_mfma_max_lds<NRs + 1>() <= kLdsPerCu) && ...);
+}
+static_assert(down_mfma_lds_fits(std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{}),
+              "the matrix-core down kernel's largest LDS must fit one CU");
+
+// Each instantiation's maximum dynamic LDS is set once per device (the
+// largest its limits allow), like the matrix-core gate/up kernel's.
+template <int... NRs>
+hipError_t down_mfma_set_lds(std::integer_sequence<int, NRs...>) {
+  hipError_t rc = hipSuccess;
+  ((rc = rc != hipSuccess ? rc
+                          : hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_down_grouped_mfma_w64<NRs + 1>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                down_mfma_max_lds<NRs + 1>())),
+   ...);
+  return rc;
+}
+
+PerDeviceOnce g_down_mfma_setup;
+hipError_t down_mfma_setup_current_device() {
+  return g_down_mfma_setup(
+      [] { return down_mfma_set_lds(std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{}); });
+}
+
+template <int NR>
+long long launch_down_mfma_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
+                             const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
+  const long long blocks = H / moe::kDownMfmaRows;   // H is a multiple of 32
+  if (!go) return blocks;
+  hipLaunchKernelGGL((moe::moe_down_grouped_mfma_w64<NR>), dim3((unsigned)blocks), dim3(64 * moe::down_mfma_waves(NR)),
+                     (unsigned)moe::down_mfma_lds_bytes(NR, E, B * k), st, static_cast<const uint16_t*>(h), ids, tw, wd, sd,
+                     static_cast<uint16_t*>(y), B, H, I, E, k);
+  return blocks;
+}
+
+template <int... NRs>
+DownLaunch pick_down_mfma_nr(int nr, std::integer_sequence<int, NRs...>) {
+  DownLaunch fn = nullptr;
+  ((nr == NRs + 1 ? (fn = launch_down_mfma_t<NRs + 1>, 0) : 0), ...);
+  return fn;
+}
+
+DownLaunch pick_down_mfma(int I) {
+  return pick_down_mfma_nr((I + 255) / 256, std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{});
+}
+
 // Variant table (graph-timed sweeps on MI355X, 128 experts, top-8, uniform
 // routing): the per-token kernel while few tokens share an expert, the
 // expert-grouped one from one slot per expert on (H = 2048, I = 768: 16
@@ -550,6 +619,11 @@ DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, in
     if (rows != ro || !down_grouped_allowed(I, (long long)B * k, B, E)) return nullptr;
     return pick_down_grouped(passes(I));
   }
+  if (variant == MOE_DOWN_EXPERT_GROUPED_MFMA) {
+    if (rows == 0) rows = moe::kDownMfmaRows;
+    if (rows != moe::kDownMfmaRows || !down_mfma_allowed(I, (long long)B * k, E)) return nullptr;
+    return pick_down_mfma(I);
+  }
   return nullptr;
 }
 
@@ -567,6 +641,7 @@ int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t*
     return MOE_ERR_ALIAS;
   DownLaunch fn = down_launcher(variant, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
+  if (variant == MOE_DOWN_EXPERT_GROUPED_MFMA && down_mfma_setup_current_device() != hipSuccess) return MOE_ERR_LAUNCH;
   (void)hipGetLastError();
   fn(true, static_cast<hipStream_t>(stream), h, ids, tw, wd, sd, y, B, H, I, E, k);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
