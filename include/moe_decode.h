@@ -147,8 +147,11 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     (exact) before the chunks are summed.  Same outputs within the same
  *     tolerance; requires B*k <= 1024, E <= 1024 and I <= 2048
  *     (rows_per_wave must be 0 or 8).
- * The plain call takes the grouped variant once B*k >= E (an average of one
- * or more slots per expert) and the limits allow it, else the per-token one. */
+ * The plain call takes the matrix-core grouped variant once 4*B*k >= 3E
+ * (0.75 slots per expert on average), or 2*B*k >= E for I > 1024, and its
+ * limits allow it; where they do not, the vector-unit grouped variant once
+ * B*k >= E; else the per-token one: the fastest in each measured
+ * configuration. */
 #define MOE_DOWN_PER_TOKEN 1
 #define MOE_DOWN_EXPERT_GROUPED 2
 #define MOE_DOWN_EXPERT_GROUPED_MFMA 3

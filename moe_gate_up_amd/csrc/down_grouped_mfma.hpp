@@ -47,10 +47,12 @@ constexpr int kDownMfmaRows = 8;        // output dimensions per workgroup: 2 ro
 constexpr int kDownMfmaUnitSlots = 8;   // slots per work unit (2 groups of 4 MFMA columns)
 constexpr int kDownMfmaMaxRounds = 8;   // I <= 8 rounds of 256 elements
 
-// Launch shape by rounds of 256 elements over I: 16 wavefronts per workgroup
-// while a wavefront fits 128 VGPRs (I <= 768), else 8, and 6 from 7 rounds on
-// so that the stages fit LDS (160 KB per CU).
-__host__ __device__ constexpr int down_mfma_waves(int nr) { return nr <= 3 ? 16 : (nr <= 6 ? 8 : 6); }
+// Launch shape by rounds of 256 elements over I (graph-timed on MI355X, H =
+// 2048, I = 768, 32 tokens): 12 wavefronts per workgroup up to 3 rounds (34.4
+// us against 35.6 with 16 and 35.2 with 8; more units in flight per CU only
+// lengthen the queues), 8 up to 6 rounds, 6 beyond so that the stages fit LDS
+// (160 KB per CU).
+__host__ __device__ constexpr int down_mfma_waves(int nr) { return nr <= 3 ? 12 : (nr <= 6 ? 8 : 6); }
 // Each wavefront stages its unit's 8 rows in LDS, each row padded to whole
 // rounds of 256 bytes.
 __host__ __device__ constexpr int down_mfma_stage_bytes(int nr) { return kDownMfmaRows * 256 * nr; }

@@ -591,14 +591,22 @@ DownLaunch pick_down_mfma(int I) {
   return pick_down_mfma_nr((I + 255) / 256, std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{});
 }
 
-// Variant table (graph-timed sweeps on MI355X, 128 experts, top-8, uniform
-// routing): the per-token kernel while few tokens share an expert, the
-// expert-grouped one from one slot per expert on (H = 2048, I = 768: 16
-// tokens 27.1 vs 28.6 us, 24 tokens 32.7 vs 38.0, 8 tokens 19.1 vs 18.2;
-// H = 4096, I = 1536: 16 tokens 105 vs 116 us, 8 tokens 65.6 vs 65.0).
+// Variant table (graph-timed sweeps of the down kernel alone on MI355X, 128
+// experts, top-8, uniform routing): the per-token kernel while few tokens
+// share an expert, the matrix-core grouped one from 0.75 slots per expert on
+// (H = 2048, I = 768: 8 tokens 17.8 per-token vs 18.0 us, 12 tokens 22.8 vs
+// 22.2, 32 tokens 45.5 vs 34.5; the vector-unit grouped kernel 38.6) or from
+// half a slot at I > 1024 (H = 4096, I = 1536: 4 tokens 37.5 vs 41.7, 8
+// tokens 65.1 vs 63.1, 64 tokens 362.6 vs 167.4, vector-unit grouped 228.3).
+// Skewed routing favours the grouped kernels earlier (16 tokens, Zipf: 24.1
+// per-token, 20.3 on the matrix cores).  The vector-unit grouped kernel is the
+// choice from one slot per expert where the matrix-core kernel's limits
+// exclude the shape.
 int down_default_variant(int B, int H, int I, int E, int k) {
   (void)H;
   const long long slots = (long long)B * k;
+  if ((4 * slots >= 3LL * E || (I > 1024 && 2 * slots >= E)) && down_mfma_allowed(I, slots, E))
+    return MOE_DOWN_EXPERT_GROUPED_MFMA;
   if (slots >= E && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
   return MOE_DOWN_PER_TOKEN;
 }

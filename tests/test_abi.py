@@ -202,14 +202,20 @@ def test_plans():
     assert mg.moe_decode_gate_up_plan(31, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
-    for B in (1, 8, 16, 32, 64):
+    for B in (1, 8, 11, 12, 16, 32, 64, 100):
         v, r, g = mg.moe_decode_down_plan(B, 2048, 768, 128, 8)
         if v == mg.MOE_DOWN_PER_TOKEN:     # one wavefront per (tile, token)
             assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * B // 4)
         else:                              # one workgroup per 8 output dimensions
-            assert v == mg.MOE_DOWN_EXPERT_GROUPED and r == 8 and g == 2048 // 8
-        assert (v == mg.MOE_DOWN_EXPERT_GROUPED) == (B * 8 >= 128)
-    assert mg.moe_decode_down_plan(100, 2048, 768, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN   # B > 64
+            assert v == mg.MOE_DOWN_EXPERT_GROUPED_MFMA and r == 8 and g == 2048 // 8
+        # on the matrix cores from 0.75 slots per expert on
+        assert (v == mg.MOE_DOWN_EXPERT_GROUPED_MFMA) == (4 * B * 8 >= 3 * 128)
+    # I > 1024: from half a slot per expert
+    assert mg.moe_decode_down_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_EXPERT_GROUPED_MFMA
+    assert mg.moe_decode_down_plan(7, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN
+    # beyond the matrix-core kernel's limits (I > 2048 rounds): the vector-unit grouped kernel, else per token
+    assert mg.moe_decode_down_plan(150, 2048, 768, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN    # B*k > 1024
+    assert mg.moe_decode_down_plan(16, 2048, 768, 1100, 8)[0] == mg.MOE_DOWN_PER_TOKEN   # E > 1024
     with pytest.raises(mg.MoeDecodeError):
         mg.moe_decode_gate_up_plan(1, 100, 768, 128, 8)
 
