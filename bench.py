@@ -342,7 +342,7 @@ def main():
             dnb = sum(d["down"] for d in pick)
             res.update(gate_up_us=t_gu / n * 1e6, down_us=t_dn / n * 1e6,
                        gate_up_GBps=gub / t_gu / 1e9, down_GBps=dnb / t_dn / 1e9,
-                       gate_up_bytes_per_launch=gub / n)
+                       gate_up_bytes_per_launch=gub / n, down_bytes_per_launch=dnb / n)
         return res
 
     def brief(r, keys=("B", "us_per_layer", "us_per_step", "GBps", "frac_of_copy_peak", "distinct_experts",
@@ -495,19 +495,28 @@ def main():
         log(f"cpu oracle ({model}): {cpu['value']} GB/s on {cores} threads ({spent / n * 1e3:.1f} ms/layer); "
             f"1 thread {s1_spent * 1e3:.0f} ms/layer")
 
-    traffic = measured_traffic("gate_up")
+    # roofline position of both kernels at the headline (HBM-bound: algorithmic bytes
+    # per launch / event-timed launch duration, against the published 8 TB/s); the
+    # dominant one (gate/up, 2/3 of the bytes) is `roofline`
     gu_variant = mg.moe_decode_gate_up_plan(B, H, I, E, k)[0]
-    roof = {
-        "bound": "hbm",
-        "kernel": {mg.MOE_GATE_UP_PER_SLOT: "moe_gate_up_3d_batched_w64",
-                   mg.MOE_GATE_UP_EXPERT_GROUPED: "moe_gate_up_expert_grouped_w64",
-                   mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA: "moe_gate_up_grouped_mfma_w64"}[gu_variant],
-        "achieved": round(kern["gate_up_GBps"], 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(kern["gate_up_GBps"] / HBM_PEAK_GBPS, 4),
-        "traffic": traffic,
+    dn_variant = mg.moe_decode_down_plan(B, H, I, E, k)[0]
+    names = {
+        "gate_up": {mg.MOE_GATE_UP_PER_SLOT: "moe_gate_up_3d_batched_w64",
+                    mg.MOE_GATE_UP_EXPERT_GROUPED: "moe_gate_up_expert_grouped_w64",
+                    mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA: "moe_gate_up_grouped_mfma_w64"}[gu_variant],
+        "down": {mg.MOE_DOWN_PER_TOKEN: "moe_down_3d_batched_w64",
+                 mg.MOE_DOWN_EXPERT_GROUPED: "moe_down_expert_grouped_w64",
+                 mg.MOE_DOWN_EXPERT_GROUPED_MFMA: "moe_down_grouped_mfma_w64"}[dn_variant],
     }
+
+    def roofline(which):
+        gbps = kern[f"{which}_GBps"]
+        return {"bound": "hbm", "kernel": names[which], "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(which),
+                "algorithmic_bytes_per_launch": round(kern[f"{which}_bytes_per_launch"]),
+                "us_per_launch": round(kern[f"{which}_us"], 3)}
+
+    roof = roofline("gate_up")
     out = {
         "metric": METRIC,
         "value": round(main_res["GBps"], 1),
@@ -539,6 +548,7 @@ def main():
                               "frac_of_copy_peak": round(vec["GBps"] / copy_gbps, 4),
                               "kernels": "moe_gate_up_expert_grouped_w64 + moe_down_expert_grouped_w64"},
         "roofline": roof,
+        "roofline_down": roofline("down"),
         "cpu_baseline": cpu,
         "sweep": sweep,
         **extra,
