@@ -5,10 +5,14 @@ accuracy A/B against warp decode on the GPU.
 The conventional path quantises x and h to MXFP8.  x's codes are a function
 of bf16 inputs only, so they match the oracle exactly; h is rounded to bf16
 after an FP32 (GPU) or FP64 (oracle) sum, so a few h values differ by one bf16
-step and may move an E4M3 code by one step.  The bar is therefore statistical
-for y: per-token cosine >= 0.9999, median error within 2e-3 + 1e-2 |ref|,
-and at most 1 % of elements outside that band (the warp-decode kernels meet
-the strict bar elsewhere).
+step and may move an E4M3 code by one step.  End to end, the bar is therefore
+statistical for y: per-token cosine >= 0.9999, median error within 2e-3 +
+1e-2 |ref|, and at most 1 % of elements outside that band.  Stage by stage
+(test_conventional_stage_by_stage), each stage is checked against its own
+definition given the GPU's output of the stage before: bit for bit where the
+stage is a function of integers or bf16 values alone (routing, the MXFP8
+quantisation of x and of the GPU's intermediate, the scatter), the layer's
+strict bar for the two products and the combine.
 """
 import numpy as np
 import pytest
@@ -137,3 +141,119 @@ def test_accuracy_ab_on_gpu(dev, B):
     print(f"B={B}: relative error vs full precision: warp decode {e_wd:.3e}, conventional {e_cv:.3e}, "
           f"ratio {e_cv / e_wd:.2f}", flush=True)
     assert 1.0 < e_cv / e_wd < 4.0
+
+
+def _conv_layout(B, H, I, E, k):
+    """Byte offsets of the conventional path's workspace parts (the order and
+    256-byte rounding moe_decode_conventional uses: route metadata, row ->
+    slot, row -> expert, slot -> row, x codes and scales, gather-buffer codes
+    and scales, bf16 intermediate, its codes and scales, per-expert outputs)."""
+    S = B * k
+    P = 2 * S
+    parts = [("meta", 4 * (3 * E + 1)), ("row_slot", 4 * P), ("row_expert", 4 * P), ("slot_row", 4 * S),
+             ("xq", B * H), ("xs", B * H // 32), ("xg", P * H), ("xgs", P * H // 32), ("hb", P * I * 2),
+             ("hq", P * I), ("hs", P * I // 32), ("ob", P * H * 2)]
+    off, o = {}, 0
+    for name, n in parts:
+        off[name] = o
+        o += (n + 255) // 256 * 256
+    off["total"] = o
+    return off
+
+
+def _mx_values(codes, scales):
+    """Values of E4M3 codes with one E8M0 scale per 32 consecutive codes (the oracle's decoders)."""
+    t4 = np.array([oracle.e4m3(q) for q in range(256)])
+    t8 = np.array([oracle.e8m0(v) for v in range(256)])
+    return t4[codes] * np.repeat(t8[scales], 32)
+
+
+@pytest.mark.parametrize("shape", [(5, 256, 64, 8, 2), (8, 2048, 768, 128, 8)], ids=["small", "S1 B=8"])
+def test_conventional_stage_by_stage(dev, shape):
+    """Each stage of the conventional path against its own definition, given the
+    GPU's output of the stage before ("Accuracy improvement": BF16 activations
+    converted to MXFP8; "The traditional MoE path": route, pad, scatter, per-row
+    GEMMs, per-expert buffers, combine).  Stages that are a function of integers
+    or bf16 values alone are checked bit for bit: the route (counts, padded
+    offsets, row <-> slot maps), the MXFP8 quantisation of x (values equal the
+    oracle's MX quantise-dequantise of bf16 x), the scatter, and the MXFP8
+    quantisation of the GPU's own bf16 intermediate.  The two products (FP32 on
+    the GPU, FP64 in the oracle) and the combine are held to the layer's bar."""
+    from oracle.compare import parity, passes
+    B, H, I, E, k = shape
+    L = mi.make_layer(310 + B, H, I, E)
+    x = mi.make_x(311, B, H)
+    ids, w = mi.route_uniform(312, B, E, k)
+    W = _weights(L, dev)
+    lay = _conv_layout(B, H, I, E, k)
+    assert lay["total"] == mg.moe_decode_conventional_workspace(B, H, I, E, k)
+    ws = torch.full((lay["total"],), 0xA5, dtype=torch.uint8, device=dev)
+    y = torch.empty((B, H), dtype=torch.int16, device=dev)
+    mg.moe_decode_conventional(_t(x, dev), _t(ids, dev), _t(w, dev), *W, y, ws)
+    torch.cuda.synchronize()
+    wsb = ws.cpu().numpy()
+    part = lambda name, n, dt=np.uint8: wsb[lay[name]:lay[name] + n * np.dtype(dt).itemsize].view(dt)
+    S, P = B * k, 2 * B * k
+
+    # 1. route: counts, power-of-two padded lists back to back, row <-> slot maps
+    meta = part("meta", 3 * E + 1, np.int32)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    pad = np.array([0 if c == 0 else 1 << int(np.ceil(np.log2(c))) for c in counts])
+    assert np.array_equal(meta[:E], counts)
+    assert np.array_equal(meta[E:2 * E], np.concatenate([[0], np.cumsum(pad)[:-1]]))
+    assert meta[3 * E] == pad.sum()
+    n_rows = int(pad.sum())
+    row_slot, row_expert = part("row_slot", P, np.int32), part("row_expert", P, np.int32)
+    slot_row = part("slot_row", S, np.int32)
+    flat = ids.ravel()
+    assert np.array_equal(row_slot[slot_row], np.arange(S))
+    assert np.array_equal(row_expert[slot_row], flat)
+    for e in range(E):   # each expert's list: its slots, then padding rows (-1)
+        rows = np.arange(meta[E + e], meta[E + e] + pad[e])
+        assert np.all(row_expert[rows] == e)
+        assert sorted(row_slot[rows][row_slot[rows] >= 0].tolist()) == np.nonzero(flat == e)[0].tolist()
+        assert np.sum(row_slot[rows] < 0) == pad[e] - counts[e]
+
+    # 2. x -> MXFP8: the values are the oracle's MX quantise-dequantise of bf16 x
+    xq, xs = part("xq", B * H), part("xs", B * H // 32)
+    got = _mx_values(xq, xs)
+    ref = oracle.mx_fake_quant(oracle.bf16_to_f64(x).ravel())
+    assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:10]
+
+    # 3. scatter: row p holds the codes and scales of its slot's token, padding rows zeros and code 127
+    xg, xgs = part("xg", P * H).reshape(P, H), part("xgs", P * H // 32).reshape(P, H // 32)
+    for p in range(n_rows):
+        s = row_slot[p]
+        if s >= 0:
+            assert np.array_equal(xg[p], xq.reshape(B, H)[s // k]) and np.array_equal(xgs[p], xs.reshape(B, -1)[s // k])
+        else:
+            assert not xg[p].any() and np.all(xgs[p] == 127)
+
+    # 4. gate/up per row against the oracle on the quantised activations (exactly bf16 values)
+    hb = part("hb", P * I, np.uint16).reshape(P, I)
+    xt = np.array([oracle.bf16_rne(v) for v in ref], np.uint16).reshape(B, H)
+    h_ref = oracle.gate_up(xt, ids, L.w_gate, L.s_gate, L.w_up, L.s_up)
+    p_h = parity(hb[slot_row].reshape(B, k, I), h_ref, S)
+    assert passes(p_h) and p_h["n_diff"] <= max(8, p_h["n"] // 200), p_h
+
+    # 5. h -> MXFP8, a function of the GPU's bf16 intermediate alone
+    hq, hs = part("hq", P * I).reshape(P, I), part("hs", P * I // 32).reshape(P, -1)
+    got = _mx_values(hq[:n_rows].ravel(), hs[:n_rows].ravel())
+    ref_h = oracle.mx_fake_quant(oracle.bf16_to_f64(hb[:n_rows]).ravel())
+    assert np.array_equal(got, ref_h)
+
+    # 6. down per row into the bf16 per-expert buffer, against the oracle on the GPU's quantised h
+    ob = part("ob", P * H, np.uint16).reshape(P, H)
+    ht = np.array([oracle.bf16_rne(v) for v in ref_h], np.uint16).reshape(n_rows, 1, I)
+    real = row_slot[:n_rows] >= 0
+    o_ref = oracle.down(ht[real], row_expert[:n_rows][real].reshape(-1, 1), np.ones((int(real.sum()), 1), np.float32),
+                        L.w_down, L.s_down)
+    p_o = parity(ob[:n_rows][real], o_ref, int(real.sum()))
+    assert passes(p_o) and p_o["n_diff"] <= max(8, p_o["n"] // 200), p_o
+
+    # 7. combine: y[b] = bf16(sum_j w[b,j] * out[row(b,j)]) from the GPU's per-expert outputs
+    obv = oracle.bf16_to_f64(ob)
+    yc = np.einsum("bk,bkh->bh", w.astype(np.float64), obv[slot_row].reshape(B, k, H))
+    y_ref = np.array([oracle.bf16_rne(v) for v in yc.ravel()], np.uint16).reshape(B, H)
+    p_y = parity(y.cpu().numpy().view(np.uint16), y_ref, B)
+    assert passes(p_y) and p_y["n_diff"] <= max(8, p_y["n"] // 200), p_y
