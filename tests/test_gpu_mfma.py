@@ -267,3 +267,19 @@ def test_two_host_threads_two_streams(dev, s1):
         ref = oracle.gate_up(x, ids, D.L.w_gate, D.L.s_gate, D.L.w_up, D.L.s_up)
         p = parity(h, ref, ids.size)
         assert passes(p), p
+
+
+@pytest.mark.parametrize("n_experts", [11, 16, 21], ids=["last round 16 items", "last round 256", "last round 496"])
+def test_partial_last_round(dev, s1, n_experts):
+    """Two tokens routed so that exactly n_experts experts are used: 48 items per
+    expert over a grid of 512, so the last round of the persistent grid holds
+    16, 256 or 496 items.  Against the oracle, twice, bit-identical."""
+    B, k = 2, 8
+    ids = np.array([list(range(8)), list(range(n_experts - 8, n_experts))], np.int32)
+    _, w = mi.route_uniform(870, B, s1.E, k)
+    x = mi.make_x(871, B, s1.H)
+    h, y = run_gpu(s1, x, ids, w, dev, variant=MFMA)
+    h_ref, y_ref = oracle.layer(x, ids, w, *s1.host())
+    check(h, y, h_ref, y_ref, B, k, f"mfma last round, {n_experts} experts", own=(s1, ids, w))
+    h2, y2 = run_gpu(s1, x, ids, w, dev, variant=MFMA)
+    assert np.array_equal(h, h2) and np.array_equal(y, y2)
