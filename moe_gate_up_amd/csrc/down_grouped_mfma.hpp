@@ -144,8 +144,9 @@ __global__ __launch_bounds__(64 * down_mfma_waves(NR)) void moe_down_grouped_mfm
     typedef __attribute__((address_space(3))) void lds_void;
     const uint32_t row0 = (uint32_t)e * (uint32_t)H + (uint32_t)o0;   // wave-uniform
 #pragma unroll
-    for (int t = 0; t < NSW; ++t)   // past the end of s_down: range-checked, reads zero
-      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, 256u * t + 4u * lane, row0 * (uint32_t)nblk, 0));
+    for (int t = 0; t < NSW; ++t)   // past the end of s_down: range-checked, reads zero (the range
+      // check covers the vector offset only, so the whole offset goes there)
+      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
 #pragma unroll
     for (int t = 0; t < 2 * NR; ++t) {   // 8 rows x PR pieces = 2 NR instructions of 64 pieces
       const int P = 64 * t + lane;

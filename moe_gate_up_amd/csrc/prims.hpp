@@ -28,6 +28,9 @@ struct alignas(16) u32x4 {
 // 32-bit offset, so no per-lane 64-bit address arithmetic is needed.  (The
 // third dword selects a 32-bit data format, as raw buffer loads on gfx9-family
 // chips require.)  Offsets must stay below 2^32; the host checks tensor sizes.
+// The range check (a load past the size reads zero) covers the per-lane
+// offset only, not the wave-uniform one: a load that relies on it puts its
+// whole offset in the per-lane operand.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
