@@ -181,108 +181,121 @@ __global__ __launch_bounds__(64 * down_mfma_waves(NR)) void moe_down_grouped_mfm
   };
 
   // One work unit (up to 8 slots of one routed expert) with its expert's rows
-  // already requested.
+  // already requested.  Both groups' h (slots 0-3 and 4-7) are requested
+  // before any product: requested after the first group's products, the
+  // second group's waited a whole L2 round trip per unit (at 64 tokens, where
+  // most units have more than 4 slots, the down kernel ran 44.2 us against
+  // 37.6 with no h loads at all).
+  static_assert(kDownMfmaUnitSlots == 8, "two groups of 4 slot columns per unit");
+  // the lane's slot column of group m0 (past the unit's end: the last slot again, unused), its h and weight
+  auto load_group = [&](int first, int count, int m0, uint32_t& sl, u32x4 (&hv)[NR][2], float& wsl) {
+    sl = si.sorted[first + min(m0 + lj, count - 1)] & 0xFFFFu;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      hv[r][0] = bload16(hr, sl * (uint32_t)I * 2u + koff[r] * 2u, 0);
+      hv[r][1] = bload16(hr, sl * (uint32_t)I * 2u + koff[r] * 2u + 16u, 0);
+    }
+    wsl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(twr, sl * 4u, 0, 0));
+  };
+  // the products of slot columns m0 .. m0 + 3 and their contributions
+  auto group = [&](int first, int count, int m0, const uint32_t (&sc)[2][NR], uint32_t sl, const u32x4 (&hv)[NR][2],
+                   float wsl) {
+    // rows whose chunks hold the NaN scale code
+    uint32_t nan_rows = 0;
+    if (m0 == 0) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        uint64_t nl = 0;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) nl |= nan_scale_lanes(sc[g][r]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nan_rows |= (uint32_t)((nl & (0x1111111111111111ull << j)) != 0) << (4 * g + j);
+      }
+    }
+
+    float acc[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const u32x4 wv = stage_read(g, r);
+        f32x4_v c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x4_t hb = as_bf16x4(hv[r][m >> 1].v[2 * (m & 1)], hv[r][m >> 1].v[2 * (m & 1) + 1]);
+          c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(hb, e4m3x4_to_bf16x4(wv.v[m]), c, 0, 0, 0);
+        }
+        // lane 4b + j, register i: chunk b of row 4g + j against slot column i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] += apply_e8m0(c[i], sc[g][r], kbias[r]);
+      }
+      // round by round: the compiler would otherwise convert every round's
+      // rows first and hold them all (128 VGPRs at I = 768 instead of ~100)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // sum the 16 chunks: values v = (g, i); lanes 32..63 keep g = 1, then
+    // odd rows keep i = 2, 3; the 4 lanes of each (g, i pair, j) hold the sum
+    float v[8];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * g + i] = acc[g][i];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      permlane32_swap(v[t], v[t + 4]);
+      v[t] += v[t + 4];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      permlane16_swap(v[t], v[t + 2]);
+      v[t] += v[t + 2];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      v[t] += dpp<0x128>(v[t]);   // row_ror:8: lane ^ 8 within the row
+      v[t] += dpp<0x124>(v[t]);   // row_ror:4: with the above, the 4 lanes l, l+4, l+8, l+12 of the row
+    }
+    // slot ids and router weights of the 4 columns (lanes 0..3 hold them)
+    uint32_t s_id[4];
+    float s_w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_id[i] = (uint32_t)__builtin_amdgcn_readlane((int)sl, i);
+      s_w[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsl), i));
+    }
+    if ((lane & 12) == 0) {   // lane 32 g + 16 p + j writes rows 4 g + j of slot columns 2 p, 2 p + 1
+      const int g = lane >> 5, p = (lane >> 4) & 1;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i = 2 * p + t;
+        if (m0 + i < count) {
+          const uint32_t s = i == 0 ? s_id[0] : (i == 1 ? s_id[1] : (i == 2 ? s_id[2] : s_id[3]));
+          const float ww = i == 0 ? s_w[0] : (i == 1 ? s_w[1] : (i == 2 ? s_w[2] : s_w[3]));
+          contrib[s * RO + 4 * g + lj] = ww * v[t];
+        }
+      }
+    }
+    // every slot of the unit carries the unit's NaN rows
+    if (m0 == 0 && lane < count) nanmask[si.sorted[first + lane] & 0xFFFFu] = nan_rows;
+  };
   auto process = [&](int un) {
     int e, first, count;   // slots si.sorted[first .. first + count), count 1 .. kDownMfmaUnitSlots
     si.unit(un, e, first, count);
     (void)e;
-    for (int m0 = 0; m0 < count; m0 += 4) {
-      // this lane's slot column (past the unit's end: the last slot again, unused)
-      const uint32_t ent = si.sorted[first + min(m0 + lj, count - 1)];
-      const uint32_t sl = ent & 0xFFFFu;
-      u32x4 hv[NR][2];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        hv[r][0] = bload16(hr, sl * (uint32_t)I * 2u + koff[r] * 2u, 0);
-        hv[r][1] = bload16(hr, sl * (uint32_t)I * 2u + koff[r] * 2u + 16u, 0);
-      }
-      const float wsl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(twr, sl * 4u, 0, 0));
-      __builtin_amdgcn_sched_barrier(0);
-
-      uint32_t sc[2][NR];
-      scale_codes(sc);
-      // rows whose chunks hold the NaN scale code
-      uint32_t nan_rows = 0;
-      if (m0 == 0) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          uint64_t nl = 0;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) nl |= nan_scale_lanes(sc[g][r]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) nan_rows |= (uint32_t)((nl & (0x1111111111111111ull << j)) != 0) << (4 * g + j);
-        }
-      }
-
-      float acc[2][4];
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const u32x4 wv = stage_read(g, r);
-          f32x4_v c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const bf16x4_t hb = as_bf16x4(hv[r][m >> 1].v[2 * (m & 1)], hv[r][m >> 1].v[2 * (m & 1) + 1]);
-            c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(hb, e4m3x4_to_bf16x4(wv.v[m]), c, 0, 0, 0);
-          }
-          // lane 4b + j, register i: chunk b of row 4g + j against slot column i
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[g][i] += apply_e8m0(c[i], sc[g][r], kbias[r]);
-        }
-        // round by round: the compiler would otherwise convert every round's
-        // rows first and hold them all (128 VGPRs at I = 768 instead of ~100)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // sum the 16 chunks: values v = (g, i); lanes 32..63 keep g = 1, then
-      // odd rows keep i = 2, 3; the 4 lanes of each (g, i pair, j) hold the sum
-      float v[8];
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * g + i] = acc[g][i];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        permlane32_swap(v[t], v[t + 4]);
-        v[t] += v[t + 4];
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        permlane16_swap(v[t], v[t + 2]);
-        v[t] += v[t + 2];
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v[t] += dpp<0x128>(v[t]);   // row_ror:8: lane ^ 8 within the row
-        v[t] += dpp<0x124>(v[t]);   // row_ror:4: with the above, the 4 lanes l, l+4, l+8, l+12 of the row
-      }
-      // slot ids and router weights of the 4 columns (lanes 0..3 hold them)
-      uint32_t s_id[4];
-      float s_w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_id[i] = (uint32_t)__builtin_amdgcn_readlane((int)sl, i);
-        s_w[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsl), i));
-      }
-      if ((lane & 12) == 0) {   // lane 32 g + 16 p + j writes rows 4 g + j of slot columns 2 p, 2 p + 1
-        const int g = lane >> 5, p = (lane >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int i = 2 * p + t;
-          if (m0 + i < count) {
-            const uint32_t s = i == 0 ? s_id[0] : (i == 1 ? s_id[1] : (i == 2 ? s_id[2] : s_id[3]));
-            const float ww = i == 0 ? s_w[0] : (i == 1 ? s_w[1] : (i == 2 ? s_w[2] : s_w[3]));
-            contrib[s * RO + 4 * g + lj] = ww * v[t];
-          }
-        }
-      }
-      // every slot of the unit carries the unit's NaN rows
-      if (m0 == 0 && lane < count) nanmask[si.sorted[first + lane] & 0xFFFFu] = nan_rows;
-    }
+    uint32_t sl0 = 0, sl1 = 0;
+    u32x4 hv0[NR][2], hv1[NR][2];
+    float w0 = 0.0f, w1 = 0.0f;
+    load_group(first, count, 0, sl0, hv0, w0);
+    if (count > 4) load_group(first, count, 4, sl1, hv1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t sc[2][NR];
+    scale_codes(sc);
+    group(first, count, 0, sc, sl0, hv0, w0);
+    if (count > 4) group(first, count, 4, sc, sl1, hv1, w1);
   };
 
   // Units are handed out as wavefronts come free.  The first unit is
