@@ -43,9 +43,11 @@
  *     null stream).  The call returns as soon as the launch is enqueued; the
  *     caller synchronises the stream before reading outputs.
  *   - Calls are thread-safe.  The only state the library keeps is set once
- *     per device, before the first launch of the matrix-core kernel on that
- *     device, and is never changed afterwards: that kernel's maximum dynamic
- *     LDS, set to the largest size its limits allow.
+ *     per device, before the first launch that needs it on that device, and
+ *     is never changed afterwards: each matrix-core kernel's maximum dynamic
+ *     LDS, set to the largest size its limits allow, and the device address
+ *     of the no-allocation entry point's scratch array (whose concurrent
+ *     calls on one device race; see moe_decode_conventional_noalloc).
  *   - Outputs are fully overwritten; every element is written exactly once.
  *   - Outputs must not overlap any input (checked on the host).
  *   - B == 0 is a valid no-op.
