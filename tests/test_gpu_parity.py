@@ -303,6 +303,13 @@ def test_batch_sweep(dev, s1, B):
     _full(s1, "batch_sweep", B, "uniform", dev, variants=BOTH)
 
 
+# the built-in table's switch points at H=2048, E=128, k=8 (down on the matrix
+# cores from 12 tokens, gate/up from 24) on either side, and the largest batches
+@pytest.mark.parametrize("B", [11, 12, 23, 48, 64])
+def test_table_switch_points_and_large_batches(dev, s1, B):
+    _full(s1, "batch_sweep", B, "uniform", dev)
+
+
 @pytest.mark.parametrize("routing", ["zipf", "adversarial", "contiguous"])
 def test_routing_stress_b32(dev, s1, routing):
     _full(s1, "routing_stress", 32, routing, dev, variants=BOTH)
