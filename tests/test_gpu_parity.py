@@ -351,6 +351,15 @@ def test_wide_layer(dev, s2, B):
         check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} variant={v}", own=(s2, ids, w))
 
 
+@pytest.mark.parametrize("B", [7, 8])
+def test_wide_layer_table_switch_point(dev, s2, B):
+    """H=4096, I=1536: the built-in table moves both kernels to the matrix
+    cores at 8 tokens; every token on either side."""
+    x, ids, w, h_ref, y_ref = wide_case(s2, B)
+    h, y = run_gpu(s2, x, ids, w, dev)
+    check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} built-in table", own=(s2, ids, w))
+
+
 # --------------------------------------------------------------- properties
 def test_output_coverage_and_guards(dev, s1):
     B, k, G = 5, 8, 4096
