@@ -103,6 +103,32 @@ def test_conventional_batch_sweep(dev, s1, B):
     check_loose(y, ref, f"conventional batch sweep B={B}")
 
 
+@pytest.mark.parametrize("routing", ["zipf", "adversarial", "contiguous"])
+def test_conventional_routing_stress(dev, s1, routing):
+    """Skewed routing gives some experts long token lists (padded to the next
+    power of two) and leaves others empty; contiguous routing gives every
+    expert exactly two tokens."""
+    L, W = s1
+    seed = mi.routing_seed("routing_stress", 32, routing)
+    x = mi.make_x(seed, 32, L.H)
+    ids, w = mi.make_routing(routing, seed, 32, L.E, 8)
+    y = run_conventional(W, x, ids, w, dev, 32, L.H, L.I, L.E, 8)
+    ref = oracle.conventional(x, ids, w, L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
+    check_loose(y, ref, f"conventional B=32 {routing}")
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_conventional_wide_layer(dev, s2, B):
+    """H=4096, I=1536: four passes of 1024 elements per gate/up row, two per down row."""
+    seed = mi.routing_seed("wide_layers", B, layer=0)
+    x = mi.make_x(seed, B, s2.H)
+    ids, w = mi.route_uniform(seed, B, s2.E, 8)
+    W = [s2.wg, s2.sg, s2.wu, s2.su, s2.wd, s2.sd]
+    y = run_conventional(W, x, ids, w, dev, B, s2.H, s2.I, s2.E, 8)
+    ref = oracle.conventional(x, ids, w, *s2.host())
+    check_loose(y, ref, f"conventional wide layer B={B}")
+
+
 def test_conventional_invalid_ids_give_nan(dev, s1):
     L, W = s1
     B, k = 4, 8
