@@ -85,3 +85,27 @@ def test_noalloc_captured_in_a_graph(dev, layer):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, eager), rep
+
+
+def test_noalloc_full_size_layer(dev):
+    """The H=2048, I=768, 128-expert layer at 32 tokens and then 4 (4.2 MiB
+    and 0.6 MiB of the 32 MiB buffer), each equal to the workspace path bit
+    for bit."""
+    s = mi.SHAPES["S1"]
+    H, I, E, k = s["H"], s["I"], s["E"], s["k"]
+    L = mi.make_layer(mi.layer_seed("single_b1"), H, I, E)
+    W = [_t(a, dev) for a in (L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)]
+    for seed, B in ((711, 32), (712, 4)):
+        print(f"noalloc full size: B={B} H={H} I={I} E={E} k={k} seed={seed}", flush=True)
+        x = _t(mi.make_x(seed, B, H), dev)
+        ids_h, w_h = mi.route_uniform(seed, B, E, k)
+        ids, w = _t(ids_h, dev), _t(w_h, dev)
+        y = torch.full((B, H), -1, dtype=torch.int16, device=dev)
+        mg.moe_decode_conventional_noalloc(x, ids, w, *W, y)
+        torch.cuda.synchronize()
+        ws = torch.empty(mg.moe_decode_conventional_workspace(B, H, I, E, k), dtype=torch.uint8, device=dev)
+        ref = torch.empty((B, H), dtype=torch.int16, device=dev)
+        mg.moe_decode_conventional(x, ids, w, *W, ref, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), (B, int((y != ref).sum()))
+        assert torch.isfinite(y.view(torch.bfloat16).float()).all()
