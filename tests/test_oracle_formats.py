@@ -128,3 +128,41 @@ def test_mx_fake_quant_properties(orc):
         assert np.all(np.abs(c - a) <= spacing / 2)
     # idempotent
     assert np.array_equal(orc.mx_fake_quant(q), q)
+
+
+def _torch_mx(v32):
+    """MX fake quantisation of float32 values in blocks of 32 through PyTorch's own
+    float8_e4m3fn conversion (round to nearest even): shared scale 2^(floor(log2
+    amax) - 8) per block (OCP MX v1.0 with E4M3's largest exponent, 8), elements
+    saturated to +-448 (torch itself does not saturate)."""
+    out = np.zeros(v32.shape, np.float64)
+    for i, blk in enumerate(v32.reshape(-1, 32)):
+        amax = float(np.abs(blk).max())
+        if amax == 0.0:
+            continue
+        X = 2.0 ** (math.floor(math.log2(amax)) - 8)
+        a = torch.from_numpy((blk.astype(np.float64) / X).astype(np.float32))   # exact: X is a power of two
+        a = a.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        out.reshape(-1, 32)[i] = a * X
+    return out
+
+
+def test_mx_fake_quant_matches_torch_e4m3(orc):
+    """The oracle's MX quantise-dequantise of activations equals PyTorch's
+    float8_e4m3fn rounding under the block's shared scale, on random float32
+    blocks over a wide range of magnitudes and on blocks built from exact ties
+    (halfway between two E4M3 values, normal and subnormal) and saturating
+    values."""
+    rng = np.random.default_rng(17)
+    v = (rng.standard_normal(32 * 256) * np.exp2(rng.integers(-30, 30, 256)).repeat(32)).astype(np.float32)
+    # a block with every element's magnitude tiny against the block max: E4M3 subnormals
+    v[:32] = (rng.standard_normal(32) * 2.0 ** -14).astype(np.float32)
+    v[0] = 300.0
+    ties = np.array([300.0, 17.0, 19.0, -17.0, 25.0, 27.0, 3.0 * 2 ** -10, 5.0 * 2 ** -10, 7.0 * 2 ** -10,
+                     -3.0 * 2 ** -10, 1.0625, 1.1875, 0.0, 2.0 ** -12, 460.0 / 512.0 * 256.0] + [1.0] * 17, np.float32)
+    sat = np.array([500.0, -510.0, 449.0, 300.0] + [2.0] * 28, np.float32)   # block max 510: X = 1, 449..510 saturate
+    v = np.concatenate([v, ties, sat])
+    got = orc.mx_fake_quant(v.astype(np.float64))
+    ref = _torch_mx(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(v[i]), float(got[i]), float(ref[i])) for i in bad[:8]]

@@ -174,3 +174,39 @@ def test_conventional_path_is_less_accurate(orc, B):
     assert e_cv > e_wd, (e_cv, e_wd)
     # the predicted ratio for quantising both GEMM inputs is about sqrt(2); only the direction is pinned
     assert 1.0 < e_cv / e_wd < 4.0
+
+
+def _exact_bf16_bits(v):
+    """bf16 bit patterns of float64 values that are bf16 values (checked)."""
+    f = np.asarray(v, np.float64).astype(np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(_bf16_vals(bits), np.asarray(v, np.float64)), "not bf16-representable"
+    return bits
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_conventional_is_the_composition_of_its_stages(orc, k):
+    """The emulated conventional path equals its stages put together from the
+    oracle's other functions (blog post, "The traditional MoE path" and
+    "Accuracy improvement"): x quantised to MXFP8, the warp-decode gate/up on
+    it, the intermediate quantised to MXFP8, each routed expert's down output
+    rounded to bf16 on its own (the per-expert buffer), and the router-weighted
+    combine rounded to bf16 once."""
+    B, H, I, E = 4, 96, 64, 5
+    L = mi.make_layer(31, H, I, E)
+    x = mi.make_x(32, B, H)
+    ids, w = mi.route_uniform(33, B, E, k)
+    args = (L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
+    y_cv = orc.conventional(x, ids, w, *args)
+    xq = _exact_bf16_bits(orc.mx_fake_quant(_bf16_vals(x)))
+    h = orc.gate_up(xq, ids, L.w_gate, L.s_gate, L.w_up, L.s_up)
+    hq = _exact_bf16_bits(orc.mx_fake_quant(_bf16_vals(h)))
+    per_expert = np.stack([_bf16_vals(orc.down(hq[:, j:j + 1], ids[:, j:j + 1], np.ones((B, 1), np.float32),
+                                               L.w_down, L.s_down)) for j in range(k)], axis=1)   # [B, k, H]
+    combine = np.zeros((B, H))
+    for j in range(k):
+        combine += w[:, j:j + 1].astype(np.float64) * per_expert[:, j]
+    y_ref = np.array([[orc.bf16_rne(v) for v in row] for row in combine], np.uint16)
+    assert np.array_equal(y_cv, y_ref), np.nonzero(y_cv != y_ref)
+    # and quantisation did something: without it the warp-decode layer differs
+    assert not np.array_equal(y_cv, orc.layer(x, ids, w, *args)[1])

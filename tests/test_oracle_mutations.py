@@ -2,7 +2,8 @@
 
 Each case copies the oracle's C source, plants one mistake in the copy (a
 dropped sign, a wrong exponent bias or index, swapped operands, a wrong
-rounding rule, a dropped router weight, a wrong tie rule in the router ...),
+rounding rule, a dropped router weight, a wrong tie rule in the router, a
+dropped quantisation step or a wrong MX rule in the conventional emulation ...),
 builds it into a temporary library, and runs the pin tests against it.  At least one pin has to fail for
 every planted mistake; the unmodified oracle passes all of them (the other test
 modules).  The planted mistakes only ever live in a temporary copy.
@@ -42,6 +43,19 @@ MUTATIONS = [
     ("router weights not renormalised", "- m) / z / s;", "- m) / z;"),
     ("router weight of the wrong slot", "w_out[b * k + j] = exp((double)l[ids_out[b * k + j]] - m)",
      "w_out[b * k + j] = exp((double)l[ids_out[b * k]] - m)"),
+    # the emulated conventional path
+    ("mx shared exponent", "X = ldexp(1.0, ex - 1 - 8);", "X = ldexp(1.0, ex - 1 - 7);"),
+    ("mx saturation dropped", "if (a > 448.0)\n                a = 448.0;", "if (a > 448.0)\n                a = a;"),
+    ("mx ties away from zero", "    return nearbyint(a / spacing) * spacing;", "    return round(a / spacing) * spacing;"),
+    ("mx subnormal spacing", "        spacing = ldexp(1.0, -9);", "        spacing = ldexp(1.0, -10);"),
+    ("mx significand width", "spacing = ldexp(1.0, ex - 1 - 3);", "spacing = ldexp(1.0, ex - 1 - 4);"),
+    ("conventional x not quantised", "        orc_mx_fake_quant(xq, H);", "        (void)0;"),
+    ("conventional h not quantised", "            orc_mx_fake_quant(hq, I);", "            (void)0;"),
+    ("per-expert buffer not rounded", "acc[o] += (double)tw[b * k + j] * orc_bf16_value(orc_bf16_rne(d));",
+     "acc[o] += (double)tw[b * k + j] * d;"),
+    ("combine weight of the wrong slot", "acc[o] += (double)tw[b * k + j] * orc_bf16_value(orc_bf16_rne(d));",
+     "acc[o] += (double)tw[b * k] * orc_bf16_value(orc_bf16_rne(d));"),
+    ("conventional x of the wrong token", "xq[c] = orc_bf16_value(x[b * H + c]);", "xq[c] = orc_bf16_value(x[c]);"),
 ]
 
 PINS = [
@@ -57,6 +71,8 @@ PINS = [
     ("linearity", lambda o: L.test_router_weight_linearity_and_special_cases(o)),
     ("router ranks", lambda o: RT.test_route_matches_rank_definition(o, 12, 5)),
     ("router k=2", lambda o: RT.test_route_k2_is_logistic_of_the_gap(o)),
+    ("mx vs torch", lambda o: F.test_mx_fake_quant_matches_torch_e4m3(o)),
+    ("conventional composition", lambda o: L.test_conventional_is_the_composition_of_its_stages(o, 3)),
 ]
 
 
