@@ -210,3 +210,30 @@ def test_conventional_is_the_composition_of_its_stages(orc, k):
     assert np.array_equal(y_cv, y_ref), np.nonzero(y_cv != y_ref)
     # and quantisation did something: without it the warp-decode layer differs
     assert not np.array_equal(y_cv, orc.layer(x, ids, w, *args)[1])
+
+
+def test_truth_layer_special_cases_and_invariants(orc):
+    """The full-precision reference of the accuracy A/B (blog post, "Accuracy
+    improvement"): with one routed expert of weight 1 it is PyTorch's own dense
+    SwiGLU FFN (F.linear and F.silu in float64) on the unquantised draws; it is
+    linear in the router weights and does not depend on the slot order."""
+    import torch.nn.functional as Fn
+    B, H, I, E, k = 3, 96, 64, 4, 3
+    L = mi.make_layer(41, H, I, E, keep_fp32=True)
+    x = mi.make_x(42, B, H)
+    xt = torch.from_numpy(_bf16_vals(x))
+    for e in range(E):
+        ids1 = np.full((B, 1), e, np.int32)
+        T = orc.truth_layer(x, ids1, np.ones((B, 1), np.float32), L.f_gate, L.f_up, L.f_down)
+        g = Fn.linear(xt, torch.from_numpy(L.f_gate[e].astype(np.float64)))
+        u = Fn.linear(xt, torch.from_numpy(L.f_up[e].astype(np.float64)))
+        ref = Fn.linear(Fn.silu(g) * u, torch.from_numpy(L.f_down[e].astype(np.float64))).numpy()
+        assert np.allclose(T, ref, rtol=1e-12, atol=1e-14)
+    ids, w = mi.route_uniform(43, B, E, k)
+    T = orc.truth_layer(x, ids, w, L.f_gate, L.f_up, L.f_down)
+    parts = [orc.truth_layer(x, ids[:, j:j + 1], np.ones((B, 1), np.float32), L.f_gate, L.f_up, L.f_down)
+             for j in range(k)]
+    assert np.allclose(T, sum(w[:, j:j + 1].astype(np.float64) * parts[j] for j in range(k)), rtol=1e-12, atol=1e-14)
+    perm = np.array([2, 0, 1])
+    Tp = orc.truth_layer(x, ids[:, perm], w[:, perm], L.f_gate, L.f_up, L.f_down)
+    assert np.allclose(T, Tp, rtol=1e-12, atol=1e-14)
