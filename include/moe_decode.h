@@ -113,14 +113,14 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     B*k <= 1024 and E <= 1024.
  *   MOE_GATE_UP_EXPERT_GROUPED_MFMA: the same grouping with the dot products
  *     on the matrix cores (v_mfma_f32_16x16x32_bf16): a workgroup takes 16
- *     neurons of one routed expert for up to 16 of its slots, streaming the
+ *     neurons of one routed expert for up to 8 or 16 of its slots, streaming the
  *     rows and activations through LDS in 512-element chunks; the E8M0 scale
  *     is folded into the E4M3 -> bf16 conversion.  Same outputs within the
  *     same tolerance; requires H a multiple of 2048 up to 8192, B*k <= 1024,
  *     E <= 1024, and s_gate, s_up 16-byte aligned (MOE_ERR_ALIGN otherwise;
  *     rows_per_wave must be 0 or 16).
- * The plain call takes the matrix-core variant from 1.5 slots per expert on
- * (2*B*k >= 3E), or from half a slot at H >= 4096 (2*B*k >= E), when its
+ * The plain call takes the matrix-core variant from one slot per expert on
+ * (B*k >= E), or from half a slot at H >= 4096 (2*B*k >= E), when its
  * limits allow (with unaligned scales it takes the vector-unit grouped
  * variant instead); where they do not, the vector-unit grouped one from two
  * slots per expert on (B*k >= 2E); else the per-slot one: the fastest in each

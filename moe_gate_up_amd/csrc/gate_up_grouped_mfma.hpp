@@ -48,16 +48,21 @@ namespace moe {
 
 constexpr int kMfmaChunk = 512;                       // reduction elements per LDS chunk
 constexpr int kMfmaRows = 16;                         // neurons per work item (MFMA rows)
-constexpr int kMfmaUnitSlots = 16;                    // slots per work unit = MFMA columns
+constexpr int kMfmaColumns = 16;                      // MFMA columns: the most slots a work unit can have
 constexpr int kMfmaSafeScale = 246;                   // 448 * 2^(246 - 127) < 2^128
 constexpr int kMfmaWBytes = 2 * kMfmaRows * kMfmaChunk;     // weight chunk: 32 rows x 512 bytes
-constexpr int kMfmaXBytes = kMfmaUnitSlots * kMfmaChunk * 2;  // activation chunk: 16 tokens x 1 KB
-constexpr int kMfmaBufBytes = kMfmaWBytes + kMfmaXBytes;
 
-// LDS: slot index | 2 chunk buffers | the scale codes of the item's 32 rows
-// (the partial sums [4 waves][2][16][16] reuse the buffer the last chunk leaves free)
-__host__ __device__ constexpr int mfma_lds_bytes(int E, int S, int H) {
-  return slot_index_lds_bytes(E, S) + 2 * kMfmaBufBytes + 2 * kMfmaRows * (H / 32);
+// One chunk buffer: the weight chunk and the unit's activations over the chunk
+// (ch tokens x 1 KB, ch = 8 or 16 slots per work unit).
+__host__ __device__ constexpr int mfma_buf_bytes(int ch) { return kMfmaWBytes + ch * kMfmaChunk * 2; }
+// LDS: the slot index's live part | 2 chunk buffers | the scale codes of the
+// item's 32 rows (the chunk buffers also cover the index build's scratch,
+// and the partial sums [4 waves][2][16][16] reuse the buffer the last chunk
+// leaves free)
+__host__ __device__ constexpr int mfma_lds_bytes(int E, int S, int H, int ch) {
+  return slot_index_live_bytes(S) + 2 * mfma_buf_bytes(ch) + 2 * kMfmaRows * (H / 32) > slot_index_lds_bytes(E, S)
+             ? slot_index_live_bytes(S) + 2 * mfma_buf_bytes(ch) + 2 * kMfmaRows * (H / 32)
+             : slot_index_lds_bytes(E, S);
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -91,17 +96,19 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ sg,
     const uint8_t* __restrict__ wu, const uint8_t* __restrict__ su,
-    uint16_t* __restrict__ h, int B, int H, int I, int E, int k) {
+    uint16_t* __restrict__ h, int B, int H, int I, int E, int k, int ch) {
   typedef __attribute__((address_space(3))) void lds_void;
   const int slots = B * k;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const SlotIndex si = build_slot_index<256, true>(lds, ids, slots, E, k, kMfmaUnitSlots);
-  uint8_t* buf = lds + slot_index_lds_bytes(E, slots);               // 2 x (weights | activations)
+  const SlotIndex si = build_slot_index<256, true>(lds, ids, slots, E, k, ch);
+  __syncthreads();   // every thread has read the build's counters: its scratch becomes chunk buffer space
+  const int bufb = mfma_buf_bytes(ch);
+  uint8_t* buf = lds + slot_index_live_bytes(slots);                 // 2 x (weights | activations)
   const int nblk = H >> 5;
-  uint8_t* scl = buf + 2 * kMfmaBufBytes;                            // [2][16 rows][nblk] codes
+  uint8_t* scl = buf + 2 * bufb;                                     // [2][16 rows][nblk] codes
 
   const uint32_t wbytes = (uint32_t)E * (uint32_t)I * (uint32_t)H;   // < 2^32, checked on the host
   const rsrc_t gr = make_rsrc(wg, wbytes), ur = make_rsrc(wu, wbytes);
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
 
   // partial sums [4][2][16][16]: in the buffer of chunk n_chunks, which no chunk
   // of the item fills after chunk n_chunks - 2 has been used
-  float* part = reinterpret_cast<float*>(buf + (n_chunks & 1) * kMfmaBufBytes);
+  float* part = reinterpret_cast<float*>(buf + (n_chunks & 1) * bufb);
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int un = __builtin_amdgcn_readfirstlane(item / n_grp);
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
     // copies of chunk c into buffer c % 2: wavefront w takes weight rows
     // 8w .. 8w + 7 (two per instruction, one matrix each) and tokens w, w + 4, ...
     auto copy_chunk = [&](int c) {
-      uint8_t* wb = buf + (c & 1) * kMfmaBufBytes;
+      uint8_t* wb = buf + (c & 1) * bufb;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int r2 = 8 * w + 2 * p;                 // rows r2, r2 + 1 (both gate or both up)
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
         }
       }
       if (c + 1 < n_chunks) copy_chunk(c + 1);
-      const uint8_t* wb = buf + (c & 1) * kMfmaBufBytes;
+      const uint8_t* wb = buf + (c & 1) * bufb;
       const uint8_t* xb = wb + kMfmaWBytes;
       // This wavefront's operands of chunk c: its tiles tl = 2w and 2w + 1 (64
       // elements each).  Lane (lr, lq) takes the 16-byte piece 4 tl + lq of gate

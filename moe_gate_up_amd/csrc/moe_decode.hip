@@ -251,23 +251,44 @@ GateUpLaunch pick_grouped(int nch, int r) {
 }
 
 // Matrix-core grouped kernel: a persistent grid of one resident round of
-// workgroups (two per CU while the LDS footprint allows, on MI355X's 256 CUs;
-// a sweep of 384 to 1024 workgroups at 32 and 64 tokens found exactly one
-// round fastest, partial rounds up to 25 % slower); dynamic LDS: the slot
-// index, two chunk buffers and the item's scale codes.
+// workgroups on MI355X's 256 CUs (a sweep of 384 to 1024 workgroups at 32 and
+// 64 tokens with two per CU found exactly one resident round fastest, partial
+// rounds up to 25 % slower); dynamic LDS: the slot index, two chunk buffers
+// and the item's scale codes.  Work units of 8 slots halve the activation
+// half of the chunk buffers; where that lets three workgroups share a CU
+// (up to ~40 tokens at H = 2048, 128 experts) it is the faster choice (32
+// tokens: 64.3 vs 65.8 us; 16 tokens: 47.9 vs 49.6; Zipf, 32 tokens: 49.0
+// vs 49.9), otherwise units of 16 slots with two workgroups per CU (64
+// tokens: 74.7 vs 75.8 us, Zipf 71.5 vs 77.1: an expert shared by more
+// tokens is cut into fewer units, each of which reads its rows).
 constexpr long long kMfmaCus = 256;
 constexpr int kLdsPerCu = 160 * 1024;
+// LDS the residency count is computed against: three workgroups of 54,272
+// bytes each (162,816 in all) did not fit one CU on MI355X, three of 53,760 did
+constexpr int kLdsPerCuUsable = kLdsPerCu - 2048;
+struct MfmaShape {
+  int ch;          // slots per work unit: 8 or 16
+  int lds;         // dynamic LDS bytes
+  long long per_cu;
+};
+MfmaShape mfma_shape(int H, long long slots, int E) {
+  const int l8 = moe::mfma_lds_bytes(E, (int)slots, H, 8);
+  if (kLdsPerCuUsable / l8 >= 3) return {8, l8, 3};
+  const int l16 = moe::mfma_lds_bytes(E, (int)slots, H, 16);
+  const long long fit = kLdsPerCuUsable / l16;
+  return {16, l16, fit > 2 ? 2 : (fit < 1 ? 1 : fit)};
+}
 bool mfma_allowed(int H, long long slots, int E) {
   return H % 2048 == 0 && H <= 8192 && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts;
 }
 
 // Largest dynamic LDS the matrix-core kernel takes within its limits (1024
-// slots over 1024 experts at H = 8192: ~92 KB).  The kernel's attribute is set
+// slots over 1024 experts at H = 8192: ~91 KB).  The kernel's attribute is set
 // to it once per device, before the first launch on that device, and never
 // changed afterwards: a per-call value would be process-wide state that a
 // concurrent call could lower between another thread's set and its launch.
 // Occupancy follows the LDS size each launch asks for, not this maximum.
-constexpr int kMfmaMaxLds = moe::mfma_lds_bytes(moe::kSortMaxExperts, moe::kSortMaxSlots, 8192);
+constexpr int kMfmaMaxLds = moe::mfma_lds_bytes(moe::kSortMaxExperts, moe::kSortMaxSlots, 8192, moe::kMfmaColumns);
 static_assert(kMfmaMaxLds <= kLdsPerCu, "the matrix-core kernel's largest LDS must fit one CU");
 
 constexpr int kMaxDevices = 64;
@@ -303,37 +324,37 @@ long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids
                       int k, const RouteIO* ro) {
   const long long slots = (long long)B * k;   // work units (<= slots) x groups of 16 neurons
   const long long items_max = slots * (long long)((I + moe::kMfmaRows - 1) / moe::kMfmaRows);
-  const int lds = moe::mfma_lds_bytes(E, (int)slots, H);
-  const long long per_cu = kLdsPerCu / lds > 2 ? 2 : (kLdsPerCu / lds < 1 ? 1 : kLdsPerCu / lds);
-  const long long blocks = items_max < kMfmaCus * per_cu ? items_max : kMfmaCus * per_cu;
+  const MfmaShape sh = mfma_shape(H, slots, E);
+  const long long blocks = items_max < kMfmaCus * sh.per_cu ? items_max : kMfmaCus * sh.per_cu;
   if (!go) return blocks;
   if (ro) {
     launch_route(st, *ro, B, E, k);
     ids = ro->ids;
   }
-  hipLaunchKernelGGL(moe::moe_gate_up_grouped_mfma_w64, dim3((unsigned)blocks), dim3(256), (unsigned)lds, st,
-                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k);
+  hipLaunchKernelGGL(moe::moe_gate_up_grouped_mfma_w64, dim3((unsigned)blocks), dim3(256), (unsigned)sh.lds, st,
+                     static_cast<const uint16_t*>(x), ids, wg, sg, wu, su, static_cast<uint16_t*>(h), B, H, I, E, k,
+                     sh.ch);
   return blocks;
 }
 
 // Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
-// experts, top-8; gate/up alone, uniform routing unless stated).  While the
-// average routed expert serves few slots, the per-slot kernel wins: it needs
-// no sort and its grid has no per-workgroup setup (16 tokens, H = 2048: 48.3
-// us against 49.7 on the matrix cores and 51.7 on the vector-unit grouped
-// kernel).  Once tokens share experts the expert-grouped product on the matrix
-// cores reads each routed row once and wins: at H = 2048 from 1.5 slots per
-// expert (24 tokens: 59.6 vs 62.7 us per-slot; 32 tokens: 65.6 vs 70.6
-// grouped and 77.7 per-slot), at H = 4096 from half a slot per expert (8
-// tokens: 114.0 vs 115.8; 16 tokens: 173.7 vs 188.4; 32 tokens: 233.5 vs
-// 268.8 grouped).  Skewed routing favours it earlier (16 tokens, H = 2048,
-// Zipf: 35.4 vs 38.4 us); the table follows uniform routing.  The vector-unit
-// grouped kernel is the choice from two slots per expert on where the
-// matrix-core kernel's limits exclude the shape.
+// experts, top-8; gate/up alone).  While the average routed expert serves
+// few slots, the per-slot kernel wins: it needs no sort and its grid has no
+// per-workgroup setup (H = 2048, per-slot against matrix cores: 8 tokens
+// 30.0 vs 32.1 us, Zipf routing 23.3 vs 24.5; 12 tokens 39.4 vs 40.5, Zipf
+// 30.7 vs 30.1).  Once tokens share experts the expert-grouped product on
+// the matrix cores reads each routed row once and wins: at H = 2048 from one
+// slot per expert (16 tokens 48.0 vs 47.9, Zipf 38.3 vs 34.3; 20 tokens 55.8
+// vs 53.9, Zipf 45.7 vs 39.8; 24 tokens 62.6 vs 58.4; 32 tokens 77.7
+// per-slot, 70.6 vector-unit grouped, 64.3 matrix cores), at H = 4096 from
+// half a slot per expert (4 tokens 66.8 vs 67.5; 8 tokens 114.0 vs 111.1;
+// 16 tokens: 188.4 vector-unit grouped vs 173.7; 32 tokens: 268.8 vs
+// 233.5).  The vector-unit grouped kernel is the choice from two slots per
+// expert on where the matrix-core kernel's limits exclude the shape.
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
-  if ((2 * slots >= 3LL * E || (H >= 4096 && 2 * slots >= E)) && mfma_allowed(H, slots, E))
+  if ((slots >= E || (H >= 4096 && 2 * slots >= E)) && mfma_allowed(H, slots, E))
     return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
   if (slots >= 2LL * E && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;

@@ -27,8 +27,12 @@ constexpr int kSortMaxSlots = 1024;     // B*k limit
 constexpr int kSortMaxExperts = 1024;   // E limit (per-expert LDS counters)
 
 __host__ __device__ constexpr int a16(int n) { return (n + 15) & ~15; }
-// LDS bytes: range ends [E] | counts [E] | slots by expert [S] | work units [S] | arrival [S] | 4 counters
+// LDS bytes: slots by expert [S] | work units [S] | range ends [E] | counts [E] | arrival [S] | 4 counters.
+// Only the first two are read after the build; a kernel may reuse the rest
+// (from slot_index_live_bytes on) once every thread has passed a barrier
+// after build_slot_index returns.
 __host__ __device__ constexpr int slot_index_lds_bytes(int E, int S) { return 2 * a16(4 * E) + 3 * a16(4 * S) + 16; }
+__host__ __device__ constexpr int slot_index_live_bytes(int S) { return 2 * a16(4 * S); }
 
 struct SlotIndex {
   int* end_;         // end of expert e's range in `sorted` (its start is end_[e] - count_[e])
@@ -56,11 +60,11 @@ __device__ SlotIndex build_slot_index(uint8_t* lds, const int32_t* __restrict__ 
   constexpr int J = (kSortMaxSlots + NT - 1) / NT;   // slots per thread, enough for kSortMaxSlots
   SlotIndex o;
   o.ch = ch;
-  o.end_ = reinterpret_cast<int*>(lds);
-  o.count_ = reinterpret_cast<int*>(lds + a16(4 * E));
-  o.sorted = reinterpret_cast<uint32_t*>(lds + 2 * a16(4 * E));
+  o.sorted = reinterpret_cast<uint32_t*>(lds);
   o.units = o.sorted + a16(4 * slots) / 4;
-  uint32_t* arrival = o.units + a16(4 * slots) / 4;
+  o.end_ = reinterpret_cast<int*>(lds + slot_index_live_bytes(slots));
+  o.count_ = reinterpret_cast<int*>(lds + slot_index_live_bytes(slots) + a16(4 * E));
+  uint32_t* arrival = reinterpret_cast<uint32_t*>(lds + slot_index_live_bytes(slots) + 2 * a16(4 * E));
   int* misc = reinterpret_cast<int*>(arrival + a16(4 * slots) / 4);   // 1: invalid slots, 2: units, 3: split experts
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -180,7 +180,7 @@ def test_conventional_noalloc_arguments():
 
 
 def test_plans():
-    for B in (1, 8, 16, 23, 24, 32, 64):
+    for B in (1, 8, 15, 16, 23, 24, 32, 42, 43, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
         if v == mg.MOE_GATE_UP_PER_SLOT:   # one wavefront per (tile, slot)
             assert r in (1, 2, 4, 8)
@@ -188,11 +188,12 @@ def test_plans():
         elif v == mg.MOE_GATE_UP_EXPERT_GROUPED:   # persistent: <= 2048 workgroups, <= the possible work items
             assert r in (1, 2, 4, 8)
             assert g == min(2048, -(-(B * 8 * -(-768 // (4 * r))) // 2))   # items taken in pairs
-        else:                              # matrix cores: one resident round, two workgroups per CU
-            assert v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA and r == 16 and g == 512
-        # on the matrix cores from 1.5 slots per expert on, per slot below
-        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (2 * B * 8 >= 3 * 128)
-        assert (v == mg.MOE_GATE_UP_PER_SLOT) == (2 * B * 8 < 3 * 128)
+        else:   # matrix cores: one resident round; three workgroups per CU while units of 8 slots fit
+            # three in LDS (B*k <= 341 slots here: the slot index grows with them), else two
+            assert v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA and r == 16 and g == (768 if B <= 42 else 512)
+        # on the matrix cores from one slot per expert on, per slot below
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (B * 8 >= 128)
+        assert (v == mg.MOE_GATE_UP_PER_SLOT) == (B * 8 < 128)
     # H = 4096: the matrix cores from half a slot per expert on
     assert mg.moe_decode_gate_up_plan(32, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
     assert mg.moe_decode_gate_up_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA

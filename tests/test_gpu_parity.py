@@ -298,14 +298,16 @@ def test_single_layer_b1(dev, s1):
     _full(s1, "single_b1", 1, "uniform", dev)
 
 
-@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 24, 32])   # 24: where the table turns to the matrix cores
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 24, 32])
 def test_batch_sweep(dev, s1, B):
     _full(s1, "batch_sweep", B, "uniform", dev, variants=BOTH)
 
 
 # the built-in table's switch points at H=2048, E=128, k=8 (down on the matrix
-# cores from 12 tokens, gate/up from 24) on either side, and the largest batches
-@pytest.mark.parametrize("B", [11, 12, 23, 48, 64])
+# cores from 12 tokens, gate/up from 16; gate/up's work units of 8 slots, three
+# workgroups per CU, up to 42 tokens, of 16 from 43) on either side, and the
+# largest batches
+@pytest.mark.parametrize("B", [11, 12, 15, 16, 42, 43, 64])
 def test_table_switch_points_and_large_batches(dev, s1, B):
     _full(s1, "batch_sweep", B, "uniform", dev)
 
