@@ -28,9 +28,12 @@
 // E8M0 scale folded in: the scaled weight rounded to bf16, exact whenever
 // it is a normal bf16.  So that no scaled weight overflows, a row whose
 // largest code exceeds 246 has all its codes lowered by d and its sums
-// multiplied by 2^d (exact); its blocks more than 2^236 below its largest
-// then round to bf16 subnormals or zero, far below FP32 resolution of the
-// sum.  NaN scale codes and E4M3 NaN codes give NaN outputs.
+// multiplied by 2^d (exact); so that the weights of a row of tiny blocks
+// stay normal, a row whose largest code is below 64 has all its codes
+// raised by d and its sums multiplied by 2^-d.  Every block within 2^54 of
+// its row's largest is then exact; blocks further below round to bf16
+// subnormals or zero, far below FP32 resolution of the sum.  NaN scale
+// codes and E4M3 NaN codes give NaN outputs.
 //
 // After the last chunk each wavefront's 16 x 16 gate and up partial sums go
 // to LDS (the chunk buffer the last chunk leaves free) and threads (n, t) add
@@ -50,6 +53,7 @@ constexpr int kMfmaChunk = 512;                       // reduction elements per 
 constexpr int kMfmaRows = 16;                         // neurons per work item (MFMA rows)
 constexpr int kMfmaColumns = 16;                      // MFMA columns: the most slots a work unit can have
 constexpr int kMfmaSafeScale = 246;                   // 448 * 2^(246 - 127) < 2^128
+constexpr int kMfmaLowScale = 64;                     // rows whose largest code is below: raised to it
 constexpr int kMfmaWBytes = 2 * kMfmaRows * kMfmaChunk;     // weight chunk: 32 rows x 512 bytes
 
 // One chunk buffer: the weight chunk and the unit's activations over the chunk
@@ -90,6 +94,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ uint32_t has_big_scale(uint32_t v) {
   const uint32_t t = ~v;
   return (t - 0x09090909u) & ~t & 0x80808080u;
+}
+// Nonzero iff a byte of v is an E8M0 code below 64 (a borrow out of a byte
+// only starts at a byte that is itself below 64).
+__device__ __forceinline__ uint32_t has_small_scale(uint32_t v) {
+  static_assert(kMfmaLowScale == 64, "the byte constant below");
+  return (v - 0x40404040u) & ~v & 0x80808080u;
 }
 
 __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
@@ -163,29 +173,32 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
 
     f32x4_t accg = {0.0f, 0.0f, 0.0f, 0.0f}, accu = {0.0f, 0.0f, 0.0f, 0.0f};
     int dg = 0, du = 0;   // this lane's row's shift (gate / up)
-    bool big = false;
+    bool shifted = false;
     const int tc = lr < count ? lr : count - 1;   // this lane's token column (past the unit: repeat, unused)
     for (int c = 0; c < n_chunks; ++c) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wavefront's copies of chunk c (and the scales)
       __syncthreads();                            // everyone's; and everyone is done with chunk c - 1
-      // codes above 246 anywhere in the item's rows (a wave-wide check), read
-      // before the copies of chunk 1 are issued so that these reads wait for nothing
+      // codes above 246 or below 64 anywhere in the item's rows (a wave-wide
+      // check), read before the copies of chunk 1 are issued so that these
+      // reads wait for nothing
       if (c == 0) {
         uint32_t any = 0;
         for (int i = lane * 16; i < 2 * kMfmaRows * nblk; i += 1024) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(scl + i);
-          any |= has_big_scale(v.v[0]) | has_big_scale(v.v[1]) | has_big_scale(v.v[2]) | has_big_scale(v.v[3]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) any |= has_big_scale(v.v[q]) | has_small_scale(v.v[q]);
         }
-        big = __builtin_amdgcn_ballot_w64(any != 0) != 0;
-        if (big) {   // this lane's rows' largest non-NaN codes
+        shifted = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+        if (shifted) {   // this lane's rows' largest non-NaN codes
           int mg = 0, mu = 0;
           for (int b = 0; b < nblk; ++b) {
             const int cg = scl[lr * nblk + b], cu = scl[(kMfmaRows + lr) * nblk + b];
             mg = (cg != 255 && cg > mg) ? cg : mg;
             mu = (cu != 255 && cu > mu) ? cu : mu;
           }
-          dg = mg > kMfmaSafeScale ? mg - kMfmaSafeScale : 0;
-          du = mu > kMfmaSafeScale ? mu - kMfmaSafeScale : 0;
+          // lowered by d > 0 or raised by -d > 0; raised codes stay below 128
+          dg = mg > kMfmaSafeScale ? mg - kMfmaSafeScale : (mg < kMfmaLowScale ? mg - kMfmaLowScale : 0);
+          du = mu > kMfmaSafeScale ? mu - kMfmaSafeScale : (mu < kMfmaLowScale ? mu - kMfmaLowScale : 0);
         }
       }
       if (c + 1 < n_chunks) copy_chunk(c + 1);
@@ -245,7 +258,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
       }
     }
     // lane l holds rows 4 (l / 16) + j of column l % 16
-    if (big) {
+    if (shifted) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rsrc = 4 * (4 * lq + j);   // lane 4 lq + j (< 16) holds that row's shifts

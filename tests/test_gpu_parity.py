@@ -155,6 +155,77 @@ def test_every_e4m3_code_through_gate_up_kernel(dev, scale, gvariant):
     assert np.all(err <= 2e-3 + 1e-2 * np.abs(ref[fin])), (scale, np.max(err))
 
 
+# Tiny block scales with activations large enough that the products are
+# ordinary numbers again: a kernel that rounded the scaled weights to bf16
+# subnormals (or flushed them) would miss by far more than the bar here, which
+# is relative only.  The bf16 activation 2^p (p <= 100, so no FP32 partial sum
+# overflows) brings dec(code) * 2^(scale - 127) * 2^p to at least 2^-36.
+TINY_SCALES = [0, 1, 5, 9, 10, 27, 54, 63, 64, 100]
+
+
+def _pow2_bf16(p):
+    return np.uint16((p + 127) << 7)
+
+
+@pytest.mark.parametrize("scale", TINY_SCALES)
+@pytest.mark.parametrize("gvariant", [mg.MOE_GATE_UP_PER_SLOT, mg.MOE_GATE_UP_EXPERT_GROUPED,
+                                      mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA])
+def test_tiny_scales_through_gate_up_kernel(dev, scale, gvariant):
+    """Every gate block of neuron n at E8M0 code `scale`, E4M3 code n in element 0
+    (the rest zero), its up row 2^-p in element 0, x = 2^p e_0: gate = dec(n) *
+    2^(scale - 127 + p), up = 1 exactly, h[n] = bf16(SiLU(gate)), checked to 1 %
+    of its own size (zero exactly); the NaN codes give NaN."""
+    E, H, I, k, B = 1, 2048, 256, 1, 1
+    p = min(100, 124 - scale)     # |gate| <= 448 / 8: SiLU stays a normal number
+    wg = np.zeros((E, I, H), np.uint8)
+    wg[0, :, 0] = np.arange(256, dtype=np.uint8)
+    sg = np.full((E, I, H // 32), scale, np.uint8)
+    wu = np.zeros((E, I, H), np.uint8)
+    wu[0, :, 0] = 0x38                   # E4M3 1.0
+    su = np.full((E, I, H // 32), 127 - p, np.uint8)
+    x = np.zeros((B, H), np.uint16)
+    x[0, 0] = _pow2_bf16(p)
+    ids = np.zeros((B, k), np.int32)
+    h = torch.empty((B, k, I), dtype=torch.int16, device=dev)
+    mg.moe_decode_gate_up(_t(x, dev), _t(ids, dev), _t(wg, dev), _t(sg, dev), _t(wu, dev), _t(su, dev), h,
+                          variant=gvariant)
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(h.cpu().numpy().view(np.uint16).ravel())
+    ref = oracle.bf16_to_f64(oracle.gate_up(x, ids, wg, sg, wu, su).ravel())
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), np.nonzero(np.isnan(got) != np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.all(np.isfinite(ref[fin])) and np.min(np.abs(ref[fin & (ref != 0)])) >= 2.0 ** -100   # normal
+    err = np.abs(got[fin] - ref[fin])
+    assert np.all(err <= 1e-2 * np.abs(ref[fin])), (scale, np.nonzero(err > 1e-2 * np.abs(ref[fin])))
+
+
+@pytest.mark.parametrize("scale", TINY_SCALES)
+@pytest.mark.parametrize("dvariant", [mg.MOE_DOWN_PER_TOKEN, mg.MOE_DOWN_EXPERT_GROUPED,
+                                      mg.MOE_DOWN_EXPERT_GROUPED_MFMA])
+def test_tiny_scales_through_down_kernel(dev, scale, dvariant):
+    """Every block of row o at E8M0 code `scale`, E4M3 code o in element 0, h =
+    2^p e_0, router weight 1: y[o] = dec(o) * 2^(scale - 127 + p), one product,
+    so exact."""
+    E, H, I, k, B = 1, 256, 768, 1, 1
+    p = min(100, 127 - scale)
+    wd = np.zeros((E, H, I), np.uint8)
+    wd[0, :, 0] = np.arange(256, dtype=np.uint8)
+    sd = np.full((E, H, I // 32), scale, np.uint8)
+    h = np.zeros((B, k, I), np.uint16)
+    h[0, 0, 0] = _pow2_bf16(p)
+    ids = np.zeros((B, k), np.int32)
+    w = np.ones((B, k), np.float32)
+    y = torch.empty((B, H), dtype=torch.int16, device=dev)
+    mg.moe_decode_down(_t(h, dev), _t(ids, dev), _t(w, dev), _t(wd, dev), _t(sd, dev), y, variant=dvariant)
+    torch.cuda.synchronize()
+    gv = oracle.bf16_to_f64(y.cpu().numpy().view(np.uint16)[0])
+    rv = oracle.bf16_to_f64(oracle.down(h, ids, w, wd, sd)[0])
+    assert np.array_equal(np.isnan(gv), np.isnan(rv))
+    ok = ~np.isnan(rv)
+    assert np.min(np.abs(rv[ok & (rv != 0)])) >= 2.0 ** -40
+    assert np.array_equal(gv[ok], rv[ok]), np.nonzero(gv != rv)
+
+
 # --------------------------------------------------------------- small shapes
 SMALL = [
     # B, H, I, E, k
