@@ -39,8 +39,9 @@
 // to LDS (the chunk buffer the last chunk leaves free) and threads (n, t) add
 // the 4 partials in wavefront order (a fixed order) and write
 // h = bf16(SiLU(g) * u).  Items go out round-robin over a grid of one
-// resident round (LDS: under 80 KB for the decode shapes, two workgroups per
-// CU).  Limits: H a multiple of 2048 up to 8192 (an item's scale codes are
+// resident round (LDS: under 54 KB with units of 8 slots for up to ~40
+// tokens at H = 2048, three workgroups per CU; under 80 KB with units of 16
+// for the other decode shapes, two per CU).  Limits: H a multiple of 2048 up to 8192 (an item's scale codes are
 // copied in whole KB pieces, one matrix per piece), B*k <= 1024, E <= 1024,
 // scale tensors 16-byte aligned.
 #pragma once
