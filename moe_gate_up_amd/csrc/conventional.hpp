@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void conv_scatter_kernel(const uint8_t* __rest
 // scaled by 2^(weight scale + activation scale - 254).  SWIGLU: two weight
 // tensors, out = SiLU(gate) * up; else out = the dot product.  Passes of
 // 1024 elements over the reduction K as in the warp-decode kernels.
-template <int NP, int R, bool SWIGLU>
+template <int NP, int R, bool SWIGLU, int CP>
 __global__ __launch_bounds__(256) void conv_gemv_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
                                                         const int* __restrict__ row_expert, const int* __restrict__ meta,
                                                         const uint8_t* __restrict__ w0, const uint8_t* __restrict__ s0,
@@ -216,11 +216,11 @@ __global__ __launch_bounds__(256) void conv_gemv_kernel(const uint8_t* __restric
     const uint32_t row = (uint32_t)(e * N + min(n0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < NP; ++c) {
-      g[r][c] = bload16(r0, off[c], row * (uint32_t)K);
-      gs[r][c] = bload8(rs0, off[c] >> 5, row * (uint32_t)nblk);
+      g[r][c] = bload16<CP>(r0, off[c], row * (uint32_t)K);
+      gs[r][c] = bload8<CP>(rs0, off[c] >> 5, row * (uint32_t)nblk);
       if constexpr (SWIGLU) {
-        u[r][c] = bload16(r1, off[c], row * (uint32_t)K);
-        us[r][c] = bload8(rs1, off[c] >> 5, row * (uint32_t)nblk);
+        u[r][c] = bload16<CP>(r1, off[c], row * (uint32_t)K);
+        us[r][c] = bload8<CP>(rs1, off[c] >> 5, row * (uint32_t)nblk);
       }
     }
   }

@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256) void moe_down_3d_batched_w64(
     const uint32_t wo = o * (uint32_t)I, so = o * (uint32_t)nb_row;
 #pragma unroll
     for (int c = 0; c < NP; ++c) {
-      w[r][c] = bload16(wr, woff[c], wo);
-      sc[r][c] = bload8(sr, soff[c], so);
+      w[r][c] = bload16<kStream>(wr, woff[c], wo);
+      sc[r][c] = bload8<kStream>(sr, soff[c], so);
     }
   }
 

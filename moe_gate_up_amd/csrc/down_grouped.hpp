@@ -99,11 +99,11 @@ __global__ __launch_bounds__(64 * down_grouped_waves(NP)) void moe_down_expert_g
     const uint32_t row0 = (uint32_t)e * (uint32_t)H + (uint32_t)o0;
 #pragma unroll
     for (int t = 0; t < NP; ++t)   // past the end of s_down: range-checked, reads zero
-      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
+      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, kStream));
 #pragma unroll
     for (int r = 0; r < RO; ++r)
 #pragma unroll
-      for (int c = 0; c < NP; ++c) wv[r][c] = bload16(wr, off[c], (row0 + r) * (uint32_t)I);
+      for (int c = 0; c < NP; ++c) wv[r][c] = bload16<kStream>(wr, off[c], (row0 + r) * (uint32_t)I);
   };
   // One work unit (up to 8 slots of one routed expert) with its expert's rows
   // already requested: its slots' h rows, dot products and accumulation.

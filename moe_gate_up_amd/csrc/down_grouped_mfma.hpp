@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * down_mfma_waves(NR)) void moe_down_grouped_mfm
 #pragma unroll
     for (int t = 0; t < NSW; ++t)   // past the end of s_down: range-checked, reads zero (the range
       // check covers the vector offset only, so the whole offset goes there)
-      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, 0));
+      sw[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(sr, row0 * (uint32_t)nblk + 256u * t + 4u * lane, 0, kStream));
 #pragma unroll
     for (int t = 0; t < 2 * NR; ++t) {   // 8 rows x PR pieces = 2 NR instructions of 64 pieces
       const int P = 64 * t + lane;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * down_mfma_waves(NR)) void moe_down_grouped_mfm
       const int pc = min(q ^ (4 * (rho & 3)), npr - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(stage + 1024 * t), 16,
                                                (uint32_t)rho * (uint32_t)I + 16u * (uint32_t)pc,
-                                               row0 * (uint32_t)I, 0, 0);
+                                               row0 * (uint32_t)I, 0, kStream);
     }
   };
   // the lane's 16 bytes of (row group g, round r) from the stage

@@ -124,10 +124,10 @@ void moe_gate_up_expert_grouped_w64(
       const uint32_t woff = row * (uint32_t)H, soff = row * (uint32_t)nblk;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        gw[r][c] = bload16(gr, off[c], woff);
-        uw[r][c] = bload16(ur, off[c], woff);
-        gsc[r][c] = bload8(gsr, off[c] >> 5, soff);
-        usc[r][c] = bload8(usr, off[c] >> 5, soff);
+        gw[r][c] = bload16<kStream>(gr, off[c], woff);
+        uw[r][c] = bload16<kStream>(ur, off[c], woff);
+        gsc[r][c] = bload8<kStream>(gsr, off[c] >> 5, soff);
+        usc[r][c] = bload8<kStream>(usr, off[c] >> 5, soff);
       }
     }
   };

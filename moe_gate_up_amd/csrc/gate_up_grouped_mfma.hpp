@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
         const uint32_t row = (uint32_t)(e * I + min(n0 + mr, I - 1));   // ragged: clamp, not stored
         const uint32_t piece = (uint32_t)((lane & 31) ^ mr);
         const uint32_t off = row * (uint32_t)H + (uint32_t)(c * kMfmaChunk) + 16u * piece;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r2 < 16 ? gr : ur, (lds_void*)(wb + r2 * kMfmaChunk), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r2 < 16 ? gr : ur, (lds_void*)(wb + r2 * kMfmaChunk), 16, off, 0, 0, kStream);
       }
       uint8_t* xb = wb + kMfmaWBytes;
       for (int m = w; m < count; m += 4) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void moe_gate_up_grouped_mfma_w64(
       const int mat = (p * 1024) / (kMfmaRows * nblk);
       const uint32_t base = (uint32_t)(e * I + n0) * (uint32_t)nblk;
       const uint32_t o = (uint32_t)(p * 1024 - mat * kMfmaRows * nblk);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(mat ? usr : gsr, (lds_void*)(scl + p * 1024), 16, base + o + 16u * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mat ? usr : gsr, (lds_void*)(scl + p * 1024), 16, base + o + 16u * lane, 0, 0, kStream);
     }
     copy_chunk(0);
 

@@ -38,18 +38,28 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
 
+// Cache policy operand of the buffer loads.  kStream sets the non-temporal
+// bit: the weight rows and their scale codes, which a decode step reads once
+// and the next step does not find in any cache, are marked as streaming data
+// so that they do not displace the activations, intermediates and ids that
+// many workgroups re-read from L2.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
 // 16 bytes at base + voff + soff.
+template <int CP = kCached>
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP);
   u32x4 o;
   o.v[0] = t[0]; o.v[1] = t[1]; o.v[2] = t[2]; o.v[3] = t[3];
   return o;
 }
 
 // One byte at base + voff + soff, zero-extended.
+template <int CP = kCached>
 __device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, CP);
 }
 
 // s_waitcnt immediate that waits until at most n (< 64) vector-memory
