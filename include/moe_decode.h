@@ -119,12 +119,12 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     same tolerance; requires H a multiple of 2048 up to 8192, B*k <= 1024,
  *     E <= 1024, and s_gate, s_up 16-byte aligned (MOE_ERR_ALIGN otherwise;
  *     rows_per_wave must be 0 or 16).
- * The plain call takes the matrix-core variant from one slot per expert on
- * (B*k >= E), or from half a slot at H >= 4096 (2*B*k >= E), when its
+ * The plain call takes the matrix-core variant from 0.625 slots per expert
+ * on (8*B*k >= 5E), or from half a slot at H >= 4096 (2*B*k >= E), when its
  * limits allow (with unaligned scales it takes the vector-unit grouped
- * variant instead); where they do not, the vector-unit grouped one from two
- * slots per expert on (B*k >= 2E); else the per-slot one: the fastest in each
- * measured configuration. */
+ * variant instead); where they do not, the vector-unit grouped one from one
+ * slot per expert on (B*k >= E), or half a slot at H >= 4096; else the
+ * per-slot one: the fastest in each measured configuration. */
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
 #define MOE_GATE_UP_EXPERT_GROUPED_MFMA 3
@@ -149,11 +149,11 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     (exact) before the chunks are summed.  Same outputs within the same
  *     tolerance; requires B*k <= 1024, E <= 1024 and I <= 2048
  *     (rows_per_wave must be 0 or 8).
- * The plain call takes the matrix-core grouped variant once 4*B*k >= 3E
- * (0.75 slots per expert on average), or 2*B*k >= E for I > 1024, and its
- * limits allow it; where they do not, the vector-unit grouped variant once
- * B*k >= E; else the per-token one: the fastest in each measured
- * configuration. */
+ * The plain call takes the matrix-core grouped variant once 16*B*k >= 5E
+ * (5/16 of a slot per expert on average) and its limits allow it, else the
+ * per-token one: the fastest in each measured configuration.  The vector-unit
+ * grouped variant runs on request only: its limits lie within the
+ * matrix-core one's, which is faster wherever both run. */
 #define MOE_DOWN_PER_TOKEN 1
 #define MOE_DOWN_EXPERT_GROUPED 2
 #define MOE_DOWN_EXPERT_GROUPED_MFMA 3

@@ -338,25 +338,27 @@ long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids
 }
 
 // Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
-// experts, top-8; gate/up alone).  While the average routed expert serves
-// few slots, the per-slot kernel wins: it needs no sort and its grid has no
-// per-workgroup setup (H = 2048, per-slot against matrix cores: 8 tokens
-// 30.0 vs 32.1 us, Zipf routing 23.3 vs 24.5; 12 tokens 39.4 vs 40.5, Zipf
-// 30.7 vs 30.1).  Once tokens share experts the expert-grouped product on
-// the matrix cores reads each routed row once and wins: at H = 2048 from one
-// slot per expert (16 tokens 48.0 vs 47.9, Zipf 38.3 vs 34.3; 20 tokens 55.8
-// vs 53.9, Zipf 45.7 vs 39.8; 24 tokens 62.6 vs 58.4; 32 tokens 77.7
-// per-slot, 70.6 vector-unit grouped, 64.3 matrix cores), at H = 4096 from
-// half a slot per expert (4 tokens 66.8 vs 67.5; 8 tokens 114.0 vs 111.1;
-// 16 tokens: 188.4 vector-unit grouped vs 173.7; 32 tokens: 268.8 vs
-// 233.5).  The vector-unit grouped kernel is the choice from two slots per
-// expert on where the matrix-core kernel's limits exclude the shape.
+// experts, top-8; gate/up alone, uniform routing unless stated).  While the
+// average routed expert serves few slots, the per-slot kernel wins: it needs
+// no sort and its grid has no per-workgroup setup (H = 2048, per-slot against
+// matrix cores: 8 tokens 27.6 vs 29.3 us, 9 tokens 30.5 vs 31.4).  Once
+// tokens share experts the expert-grouped product on the matrix cores reads
+// each routed row once and wins: at H = 2048 from 0.625 slots per expert (10
+// tokens 32.8 vs 32.8, 12 tokens 38.2 vs 37.0, 16 tokens 47.2 vs 43.5, 24
+// tokens 68.3 vs 52.6), at H = 4096 from half a slot (7 tokens 99.6 vs
+// 100.8, 8 tokens 109.3 vs 106.4).  Skewed routing favours it earlier
+// (H = 2048, 8 tokens, Zipf: 23.6 vs 22.6); the table follows uniform
+// routing.  Where the matrix-core kernel's limits exclude the shape, the
+// vector-unit grouped kernel takes over from one slot per expert, or half a
+// slot at H >= 4096 (per-slot against it: H = 2048, 12 tokens 38.2 vs 38.3,
+// 16 tokens 47.2 vs 46.8, 32 tokens 87.1 vs 64.6; H = 4096, 8 tokens 109.3
+// vs 101.0).
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
-  if ((slots >= E || (H >= 4096 && 2 * slots >= E)) && mfma_allowed(H, slots, E))
-    return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
-  if (slots >= 2LL * E && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
+  const bool wide = H >= 4096 && 2 * slots >= E;
+  if ((8 * slots >= 5LL * E || wide) && mfma_allowed(H, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
+  if ((slots >= E || wide) && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;
 }
 
@@ -613,22 +615,22 @@ DownLaunch pick_down_mfma(int I) {
 }
 
 // Variant table (graph-timed sweeps of the down kernel alone on MI355X, 128
-// experts, top-8, uniform routing): the per-token kernel while few tokens
-// share an expert, the matrix-core grouped one from 0.75 slots per expert on
-// (H = 2048, I = 768: 8 tokens 17.8 per-token vs 18.0 us, 12 tokens 22.8 vs
-// 22.2, 32 tokens 45.5 vs 34.5; the vector-unit grouped kernel 38.6) or from
-// half a slot at I > 1024 (H = 4096, I = 1536: 4 tokens 37.5 vs 41.7, 8
-// tokens 65.1 vs 63.1, 64 tokens 362.6 vs 167.4, vector-unit grouped 228.3).
-// Skewed routing favours the grouped kernels earlier (16 tokens, Zipf: 24.1
-// per-token, 20.3 on the matrix cores).  The vector-unit grouped kernel is the
-// choice from one slot per expert where the matrix-core kernel's limits
-// exclude the shape.
+// experts, top-8, uniform routing unless stated): the per-token kernel while
+// few tokens share an expert, the matrix-core grouped one from 5/16 of a slot
+// per expert on (H = 2048, I = 768: 4 tokens 11.0 per-token vs 11.5 us, 5
+// tokens 13.4 vs 13.0, 6 tokens 14.4 vs 14.4, 8 tokens 17.8 vs 16.7, 16
+// tokens 30.3 vs 24.1; H = 4096, I = 1536: 4 tokens 36.2 vs 38.5, 5 tokens
+// 44.0 vs 44.0, 6 tokens 51.8 vs 49.5, 8 tokens 66.2 vs 57.8).  Skewed
+// routing favours the grouped kernels earlier (H = 4096, 4 tokens, Zipf: 33.0
+// per-token, 31.8 on the matrix cores).  The vector-unit grouped kernel is
+// never the table's choice: every shape it takes, the matrix-core kernel
+// takes too, faster (per-token against it: H = 2048, 8 tokens 17.8 vs 17.3,
+// 16 tokens 30.3 vs 25.3; H = 4096, 8 tokens 66.1 vs 62.8); it runs on
+// request, as the vector-unit-only form of the grouped product.
 int down_default_variant(int B, int H, int I, int E, int k) {
   (void)H;
   const long long slots = (long long)B * k;
-  if ((4 * slots >= 3LL * E || (I > 1024 && 2 * slots >= E)) && down_mfma_allowed(I, slots, E))
-    return MOE_DOWN_EXPERT_GROUPED_MFMA;
-  if (slots >= E && down_grouped_allowed(I, slots, B, E)) return MOE_DOWN_EXPERT_GROUPED;
+  if (16 * slots >= 5LL * E && down_mfma_allowed(I, slots, E)) return MOE_DOWN_EXPERT_GROUPED_MFMA;
   return MOE_DOWN_PER_TOKEN;
 }
 

@@ -180,7 +180,7 @@ def test_conventional_noalloc_arguments():
 
 
 def test_plans():
-    for B in (1, 8, 15, 16, 23, 24, 32, 42, 43, 64):
+    for B in (1, 8, 9, 10, 15, 16, 23, 24, 32, 42, 43, 64):
         v, r, g = mg.moe_decode_gate_up_plan(B, 2048, 768, 128, 8)
         if v == mg.MOE_GATE_UP_PER_SLOT:   # one wavefront per (tile, slot)
             assert r in (1, 2, 4, 8)
@@ -191,30 +191,33 @@ def test_plans():
         else:   # matrix cores: one resident round; three workgroups per CU while units of 8 slots fit
             # three in LDS (B*k <= 341 slots here: the slot index grows with them), else two
             assert v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA and r == 16 and g == (768 if B <= 42 else 512)
-        # on the matrix cores from one slot per expert on, per slot below
-        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (B * 8 >= 128)
-        assert (v == mg.MOE_GATE_UP_PER_SLOT) == (B * 8 < 128)
+        # on the matrix cores from 0.625 slots per expert on, per slot below
+        assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (8 * B * 8 >= 5 * 128)
+        assert (v == mg.MOE_GATE_UP_PER_SLOT) == (8 * B * 8 < 5 * 128)
     # H = 4096: the matrix cores from half a slot per expert on
     assert mg.moe_decode_gate_up_plan(32, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
     assert mg.moe_decode_gate_up_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
     assert mg.moe_decode_gate_up_plan(7, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
-    # H not a multiple of 2048: never on the matrix cores; the vector-unit grouped kernel from two slots on
-    assert mg.moe_decode_gate_up_plan(64, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED
-    assert mg.moe_decode_gate_up_plan(31, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    # H not a multiple of 2048: never on the matrix cores; the vector-unit grouped kernel from one
+    # slot per expert (half a slot from H = 4096)
+    assert mg.moe_decode_gate_up_plan(16, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED
+    assert mg.moe_decode_gate_up_plan(15, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    assert mg.moe_decode_gate_up_plan(8, 5120, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED
+    assert mg.moe_decode_gate_up_plan(7, 5120, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(1, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     assert mg.moe_decode_gate_up_plan(200, 2048, 768, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT   # B*k > 1024
-    for B in (1, 8, 11, 12, 16, 32, 64, 100):
+    for B in (1, 4, 5, 8, 11, 12, 16, 32, 64, 100):
         v, r, g = mg.moe_decode_down_plan(B, 2048, 768, 128, 8)
         if v == mg.MOE_DOWN_PER_TOKEN:     # one wavefront per (tile, token)
             assert r in (1, 2, 4, 8) and g == -(-((2048 + r - 1) // r) * B // 4)
         else:                              # one workgroup per 8 output dimensions
             assert v == mg.MOE_DOWN_EXPERT_GROUPED_MFMA and r == 8 and g == 2048 // 8
-        # on the matrix cores from 0.75 slots per expert on
-        assert (v == mg.MOE_DOWN_EXPERT_GROUPED_MFMA) == (4 * B * 8 >= 3 * 128)
-    # I > 1024: from half a slot per expert
-    assert mg.moe_decode_down_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_EXPERT_GROUPED_MFMA
-    assert mg.moe_decode_down_plan(7, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN
-    # beyond the matrix-core kernel's limits (I > 2048 rounds): the vector-unit grouped kernel, else per token
+        # on the matrix cores from 5/16 of a slot per expert on
+        assert (v == mg.MOE_DOWN_EXPERT_GROUPED_MFMA) == (16 * B * 8 >= 5 * 128)
+    # the same at I = 1536
+    assert mg.moe_decode_down_plan(5, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_EXPERT_GROUPED_MFMA
+    assert mg.moe_decode_down_plan(4, 4096, 1536, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN
+    # beyond the matrix-core kernel's limits (which include the vector-unit grouped kernel's): per token
     assert mg.moe_decode_down_plan(150, 2048, 768, 128, 8)[0] == mg.MOE_DOWN_PER_TOKEN    # B*k > 1024
     assert mg.moe_decode_down_plan(16, 2048, 768, 1100, 8)[0] == mg.MOE_DOWN_PER_TOKEN   # E > 1024
     with pytest.raises(mg.MoeDecodeError):

@@ -375,10 +375,10 @@ def test_batch_sweep(dev, s1, B):
 
 
 # the built-in table's switch points at H=2048, E=128, k=8 (down on the matrix
-# cores from 12 tokens, gate/up from 16; gate/up's work units of 8 slots, three
+# cores from 5 tokens, gate/up from 10; gate/up's work units of 8 slots, three
 # workgroups per CU, up to 42 tokens, of 16 from 43) on either side, and the
 # largest batches
-@pytest.mark.parametrize("B", [11, 12, 15, 16, 42, 43, 64])
+@pytest.mark.parametrize("B", [4, 5, 9, 10, 42, 43, 64])
 def test_table_switch_points_and_large_batches(dev, s1, B):
     _full(s1, "batch_sweep", B, "uniform", dev)
 
@@ -424,10 +424,10 @@ def test_wide_layer(dev, s2, B):
         check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} variant={v}", own=(s2, ids, w))
 
 
-@pytest.mark.parametrize("B", [7, 8])
+@pytest.mark.parametrize("B", [4, 5, 7, 8])
 def test_wide_layer_table_switch_point(dev, s2, B):
-    """H=4096, I=1536: the built-in table moves both kernels to the matrix
-    cores at 8 tokens; every token on either side."""
+    """H=4096, I=1536: the built-in table moves down to the matrix cores at 5
+    tokens and gate/up at 8; every token on either side."""
     x, ids, w, h_ref, y_ref = wide_case(s2, B)
     h, y = run_gpu(s2, x, ids, w, dev)
     check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} built-in table", own=(s2, ids, w))
