@@ -124,7 +124,9 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  * limits allow (with unaligned scales it takes the vector-unit grouped
  * variant instead); where they do not, the vector-unit grouped one from one
  * slot per expert on (B*k >= E), or half a slot at H >= 4096; else the
- * per-slot one: the fastest in each measured configuration. */
+ * per-slot one.  At H = 4096 exactly, the vector-unit grouped variant from
+ * 5/16 of a slot per expert up to 7/4 (16*B*k >= 5E, 4*B*k < 7E).  Each
+ * choice is the fastest measured there. */
 #define MOE_GATE_UP_PER_SLOT 1
 #define MOE_GATE_UP_EXPERT_GROUPED 2
 #define MOE_GATE_UP_EXPERT_GROUPED_MFMA 3

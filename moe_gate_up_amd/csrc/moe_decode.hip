@@ -337,28 +337,34 @@ long long launch_mfma(bool go, hipStream_t st, const void* x, const int32_t* ids
   return blocks;
 }
 
-// Variant table from graph-timed sweeps on MI355X (H = 2048 and 4096, 128
-// experts, top-8; gate/up alone, uniform routing unless stated).  While the
-// average routed expert serves few slots, the per-slot kernel wins: it needs
-// no sort and its grid has no per-workgroup setup (H = 2048, per-slot against
-// matrix cores: 8 tokens 27.6 vs 29.3 us, 9 tokens 30.5 vs 31.4).  Once
-// tokens share experts the expert-grouped product on the matrix cores reads
-// each routed row once and wins: at H = 2048 from 0.625 slots per expert (10
-// tokens 32.8 vs 32.8, 12 tokens 38.2 vs 37.0, 16 tokens 47.2 vs 43.5, 24
-// tokens 68.3 vs 52.6), at H = 4096 from half a slot (7 tokens 99.6 vs
-// 100.8, 8 tokens 109.3 vs 106.4).  Skewed routing favours it earlier
-// (H = 2048, 8 tokens, Zipf: 23.6 vs 22.6); the table follows uniform
-// routing.  Where the matrix-core kernel's limits exclude the shape, the
-// vector-unit grouped kernel takes over from one slot per expert, or half a
-// slot at H >= 4096 (per-slot against it: H = 2048, 12 tokens 38.2 vs 38.3,
-// 16 tokens 47.2 vs 46.8, 32 tokens 87.1 vs 64.6; H = 4096, 8 tokens 109.3
-// vs 101.0).
+// Variant table from graph-timed sweeps on MI355X (128 experts, top-8;
+// gate/up alone, uniform routing unless stated).  While the average routed
+// expert serves few slots, the per-slot kernel wins: it needs no sort and its
+// grid has no per-workgroup setup (H = 2048, per-slot against matrix cores:
+// 8 tokens 27.6 vs 29.3 us, 9 tokens 30.5 vs 31.4).  Once tokens share
+// experts the expert-grouped product on the matrix cores reads each routed
+// row once and wins: at H = 2048 from 0.625 slots per expert (10 tokens 33.0
+// vs 33.0, 12 tokens 38.3 vs 37.2, 16 tokens 47.2 vs 43.5, 32 tokens 87.1 vs
+// 57.1), at H = 6144 and 8192 from half a slot (I = 1024, 8 tokens: 110.5
+// vs 104.4 and 142.6 vs 135.2; 5 tokens at H = 6144: 73.7 vs 76.2).  Skewed
+// routing favours it earlier (H = 2048, 8 tokens, Zipf: 23.6 vs 22.6); the
+// table follows uniform routing.  At H = 4096 the vector-unit grouped kernel
+// beats both from 5/16 of a slot per expert up to 7/4 (I = 1536, per-slot /
+// vector-unit grouped / matrix cores: 5 tokens 73.8 / 71.9 / 76.6, 8 tokens
+// 109.5 / 101.3 / 106.6, 16 tokens 198.4 / 164.2 / 169.7, 24 tokens 284.8 /
+// 207.3 / 209.7; I = 1024 alike), the matrix cores from there (28 tokens
+// 223.5 vs 215.6, 32 tokens 240.3 vs 232.7).  Where the matrix-core kernel's
+// limits exclude the shape, the vector-unit grouped kernel takes over from
+// one slot per expert, or half a slot at H >= 4096 (per-slot against it:
+// H = 2048, 12 tokens 38.3 vs 38.4, 16 tokens 47.2 vs 46.8).
 int gate_up_default_variant(int B, int H, int I, int E, int k) {
   (void)I;
   const long long slots = (long long)B * k;
+  const bool grouped_ok = grouped_allowed(passes(H), 1, slots, E);
+  if (H == 4096 && 16 * slots >= 5LL * E && 4 * slots < 7LL * E && grouped_ok) return MOE_GATE_UP_EXPERT_GROUPED;
   const bool wide = H >= 4096 && 2 * slots >= E;
   if ((8 * slots >= 5LL * E || wide) && mfma_allowed(H, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED_MFMA;
-  if ((slots >= E || wide) && grouped_allowed(passes(H), 1, slots, E)) return MOE_GATE_UP_EXPERT_GROUPED;
+  if ((slots >= E || wide) && grouped_ok) return MOE_GATE_UP_EXPERT_GROUPED;
   return MOE_GATE_UP_PER_SLOT;
 }
 

@@ -194,10 +194,15 @@ def test_plans():
         # on the matrix cores from 0.625 slots per expert on, per slot below
         assert (v == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA) == (8 * B * 8 >= 5 * 128)
         assert (v == mg.MOE_GATE_UP_PER_SLOT) == (8 * B * 8 < 5 * 128)
-    # H = 4096: the matrix cores from half a slot per expert on
-    assert mg.moe_decode_gate_up_plan(32, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
-    assert mg.moe_decode_gate_up_plan(8, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
-    assert mg.moe_decode_gate_up_plan(7, 4096, 1536, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
+    # H = 4096: the vector-unit grouped kernel from 5/16 of a slot per expert, the matrix cores from 7/4
+    for B, v in ((4, mg.MOE_GATE_UP_PER_SLOT), (5, mg.MOE_GATE_UP_EXPERT_GROUPED), (8, mg.MOE_GATE_UP_EXPERT_GROUPED),
+                 (27, mg.MOE_GATE_UP_EXPERT_GROUPED), (28, mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA),
+                 (64, mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA)):
+        assert mg.moe_decode_gate_up_plan(B, 4096, 1536, 128, 8)[0] == v, B
+    # H = 6144 and 8192: the matrix cores from half a slot per expert on
+    for H in (6144, 8192):
+        assert mg.moe_decode_gate_up_plan(8, H, 1024, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED_MFMA
+        assert mg.moe_decode_gate_up_plan(7, H, 1024, 128, 8)[0] == mg.MOE_GATE_UP_PER_SLOT
     # H not a multiple of 2048: never on the matrix cores; the vector-unit grouped kernel from one
     # slot per expert (half a slot from H = 4096)
     assert mg.moe_decode_gate_up_plan(16, 3072, 768, 128, 8)[0] == mg.MOE_GATE_UP_EXPERT_GROUPED

@@ -424,10 +424,11 @@ def test_wide_layer(dev, s2, B):
         check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} variant={v}", own=(s2, ids, w))
 
 
-@pytest.mark.parametrize("B", [4, 5, 7, 8])
+@pytest.mark.parametrize("B", [4, 5, 27, 28])
 def test_wide_layer_table_switch_point(dev, s2, B):
     """H=4096, I=1536: the built-in table moves down to the matrix cores at 5
-    tokens and gate/up at 8; every token on either side."""
+    tokens, gate/up to the vector-unit grouped kernel at 5 and to the matrix
+    cores at 28; every token on either side."""
     x, ids, w, h_ref, y_ref = wide_case(s2, B)
     h, y = run_gpu(s2, x, ids, w, dev)
     check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} built-in table", own=(s2, ids, w))
