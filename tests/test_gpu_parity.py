@@ -7,8 +7,9 @@ Covered: every E4M3 code and E8M0 edge scale through the real kernel, small
 shapes spanning several tiles with ragged tails and every rows-per-wave
 variant, 24 seeded random shapes (ragged H, I, E, k, B; both kernel families;
 uniform or skewed routing), the five synthetic workloads at full size and
-every token of their batches (the 48-layer workload on layers 1, 24 and 47,
-the 8-layer wide workload on layer 0), empty batches, out-of-range expert ids, full coverage of the outputs
+every token of their batches (the 48-layer workload on all 48 layers at 1
+token, every fourth at 8 and layers 1, 24 and 47 at 32, the 8-layer wide
+workload on layer 0), empty batches, out-of-range expert ids, full coverage of the outputs
 (sentinels and guard words), determinism and non-default streams.
 """
 import numpy as np
@@ -399,6 +400,26 @@ def test_decode_step_layers(dev, layer):
         h, y = run_gpu(D, x, ids, w, dev)
         h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
         check(h, y, h_ref, y_ref, B, 8, f"decode step layer={layer} B={B}", own=(D, ids, w))
+
+
+@pytest.mark.parametrize("group", range(6))
+def test_decode_step_every_layer(dev, group):
+    """Config 4 at full depth: every one of the 48 distinct layers (8 per
+    test), each with its own weights and its own routing, at 1 token, and
+    every fourth layer at 8 tokens too (32 tokens on layers 1, 24 and 47
+    above)."""
+    s = mi.SHAPES["S1"]
+    for layer in range(8 * group, 8 * group + 8):
+        D = DevLayer(mi.make_layer(mi.layer_seed("decode_step", layer), s["H"], s["I"], s["E"]), dev)
+        for B in ((1, 8) if layer % 4 == 0 else (1,)):
+            seed = mi.routing_seed("decode_step", B, layer=layer)
+            x = mi.make_x(seed, B, D.H)
+            ids, w = mi.route_uniform(seed, B, D.E, 8)
+            h, y = run_gpu(D, x, ids, w, dev)
+            h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
+            check(h, y, h_ref, y_ref, B, 8, f"decode step layer={layer} B={B}", own=(D, ids, w))
+        del D
+        torch.cuda.empty_cache()
 
 
 _WIDE_REF = {}
