@@ -8,8 +8,9 @@ shapes spanning several tiles with ragged tails and every rows-per-wave
 variant, 24 seeded random shapes (ragged H, I, E, k, B; both kernel families;
 uniform or skewed routing), the five synthetic workloads at full size and
 every token of their batches (the 48-layer workload on all 48 layers at 1
-token, every fourth at 8 and layers 1, 24 and 47 at 32, the 8-layer wide
-workload on layer 0), empty batches, out-of-range expert ids, full coverage of the outputs
+token, every fourth at 8 and layers 1, 24 and 47 at 32; the 8-layer wide
+workload on layer 0 at every batch size and on layers 1-7 at 1 token),
+empty batches, out-of-range expert ids, full coverage of the outputs
 (sentinels and guard words), determinism and non-default streams.
 """
 import numpy as np
@@ -443,6 +444,24 @@ def test_wide_layer(dev, s2, B):
     for v in BOTH:
         h, y = run_gpu(s2, x, ids, w, dev, variant=v)
         check(h, y, h_ref, y_ref, B, 8, f"wide layer B={B} variant={v}", own=(s2, ids, w))
+
+
+@pytest.mark.parametrize("layer", range(1, 8))
+def test_wide_every_layer(dev, layer):
+    """Config 5 at full depth: layers 1-7 of the 8 distinct wide layers (layer 0
+    is checked above at every batch size), each with its own weights and
+    routing, at 1 token, and the last one at 16 tokens too."""
+    s = mi.SHAPES["S2"]
+    D = DevLayer(mi.make_layer(mi.layer_seed("wide_layers", layer), s["H"], s["I"], s["E"]), dev)
+    for B in ((1, 16) if layer == 7 else (1,)):
+        seed = mi.routing_seed("wide_layers", B, layer=layer)
+        x = mi.make_x(seed, B, D.H)
+        ids, w = mi.route_uniform(seed, B, D.E, 8)
+        h, y = run_gpu(D, x, ids, w, dev)
+        h_ref, y_ref = oracle.layer(x, ids, w, *D.host())
+        check(h, y, h_ref, y_ref, B, 8, f"wide layer {layer} B={B}", own=(D, ids, w))
+    del D
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("B", [4, 5, 27, 28])
