@@ -123,6 +123,18 @@ def layer_bytes(ids: np.ndarray, H: int, I: int, k: int) -> dict:
     return dict(distinct=D, weights=w, total=gate_up + down, gate_up=gate_up, down=down)
 
 
+_GATE_UP_KERNELS = {1: "per-slot", 2: "vector-unit grouped", 3: "matrix-core grouped"}
+_DOWN_KERNELS = {1: "per-token", 2: "vector-unit grouped", 3: "matrix-core grouped"}
+
+
+def kernel_choice(B: int, H: int, I: int, E: int, k: int) -> str:
+    """The built-in table's kernels for this shape (what the plain calls run)."""
+    import moe_gate_up_amd as mg
+    vg = mg.moe_decode_gate_up_plan(B, H, I, E, k)[0]
+    vd = mg.moe_decode_down_plan(B, H, I, E, k)[0]
+    return f"gate_up {_GATE_UP_KERNELS.get(vg, vg)}, down {_DOWN_KERNELS.get(vd, vd)}"
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "moe_gate_up_amd", "csrc")
@@ -335,6 +347,8 @@ def main():
                    us_per_layer_p10=t10 / n * 1e6, us_per_layer_p90=t90 / n * 1e6,
                    us_per_step=t / steps * 1e6, GBps=byt / t / 1e9,
                    distinct_experts=float(np.mean([d["distinct"] for d in info])))
+        if path == "warp":
+            res["kernels"] = kernel_choice(B, H_, I_, E_, k_)
         if kernels:
             t_gu = stats(timed(gate_up, n)[0])[0]
             t_dn = stats(timed(down, n)[0])[0]
@@ -347,7 +361,7 @@ def main():
 
     def brief(r, keys=("B", "us_per_layer", "us_per_step", "GBps", "frac_of_copy_peak", "distinct_experts",
                        "gate_up_us", "down_us", "gate_up_GBps", "down_GBps", "routing", "layers",
-                       "us_per_layer_p10", "us_per_layer_p90")):
+                       "us_per_layer_p10", "us_per_layer_p90", "kernels")):
         return {kk: (round(r[kk], 4) if isinstance(r[kk], float) else r[kk]) for kk in keys if kk in r}
 
     S1 = (H, I, E, k)
@@ -371,7 +385,7 @@ def main():
         r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
         sweep.append(brief(r))
         log(f"sweep B={b}: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s ({r['frac_of_copy_peak']:.1%}); "
-            f"gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us")
+            f"gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us ({r['kernels']})")
 
     extra = {}
     if not args.no_configs:
@@ -451,7 +465,8 @@ def main():
             r["frac_of_copy_peak"] = r["GBps"] / copy_gbps
             c5.append(brief(r))
             log(f"H=4096/I=1536 B={b}: {r['us_per_layer']:.2f} us/layer, {r['GBps']:.0f} GB/s "
-                f"({r['frac_of_copy_peak']:.1%}); gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us")
+                f"({r['frac_of_copy_peak']:.1%}); gate_up {r['gate_up_us']:.2f} us, down {r['down_us']:.2f} us "
+                f"({r['kernels']})")
         extra["wide_shape_h4096_i1536"] = c5
         del wide
         torch.cuda.empty_cache()
