@@ -18,8 +18,11 @@ batches (the blog post's "Stage elimination" A/B), the top-k router step in
 front of the layer (fused into gate/up and as its own kernel), and the CPU
 oracle timed on the host as a baseline.
 
-Weights: one layer is generated on the host (seed 0) and uploaded into
-`--copies` separate device buffers; step i uses copy i mod copies, so
+Weights: one layer is generated on the host (seed 0) and uploaded; the other
+`--copies` - 1 layers (47 more for the 48-layer step, 7 for the wide shape)
+are made on the device from it, each with every weight's sign flipped by its
+own seeded random mask, so every layer holds distinct weights of the same
+distribution at its own addresses.  Step i uses layer i mod copies, so
 consecutive steps never read the same addresses and the 256 MB last-level
 cache (MALL) cannot serve a step from the previous one.
 
@@ -206,13 +209,27 @@ def main():
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     host_w = (L.w_gate, L.s_gate, L.w_up, L.s_up, L.w_down, L.s_down)
-    copies = []
     first = [up(a) for a in host_w]
-    copies.append(first)
-    for _ in range(1, args.copies):
-        copies.append([t.clone() for t in first])
+
+    def distinct(ws, n):
+        """Layer n: a copy of the layer at other addresses with every E4M3 weight's
+        sign flipped by a seeded random mask (magnitudes and scale codes kept), so
+        that every layer holds distinct weights of the same distribution.  The
+        mask is drawn 16 MB at a time, so that no large temporary sits between
+        the layers in device memory."""
+        out = [t.clone() for t in ws]
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + n)
+        for j in (0, 2, 4):   # w_gate, w_up, w_down (codes); the scale tensors stay as they are
+            flat = out[j].view(-1)
+            for o in range(0, flat.numel(), 1 << 24):
+                part = flat[o:o + (1 << 24)]
+                part.bitwise_xor_(torch.randint(0, 2, part.shape, generator=g, device=dev, dtype=torch.uint8) * 128)
+        return out
+
+    copies = [first] + [distinct(first, n) for n in range(1, args.copies)]
     torch.cuda.synchronize()
-    log(f"{args.copies} weight copies resident ({args.copies * L.nbytes / 1e9:.2f} GB)")
+    log(f"{args.copies} distinct layers resident ({args.copies * L.nbytes / 1e9:.2f} GB)")
 
     stream = torch.cuda.current_stream()
 
@@ -430,7 +447,7 @@ def main():
         extra["router_ab"] = ra
 
         # 48-layer decode step: 48 weight copies at distinct addresses, fresh routing per layer
-        deep = [copies[i % len(copies)] if i < len(copies) else [t.clone() for t in first] for i in range(48)]
+        deep = [copies[i] if i < len(copies) else distinct(first, i) for i in range(48)]
         torch.cuda.synchronize()
         c4 = []
         for b in (1, 8, 32):
@@ -455,7 +472,7 @@ def main():
         L2 = mi.make_layer(mi.layer_seed("wide_layers", 0), S2d["H"], S2d["I"], S2d["E"])
         wide = [[up(a) for a in (L2.w_gate, L2.s_gate, L2.w_up, L2.s_up, L2.w_down, L2.s_down)]]
         del L2
-        wide += [[t.clone() for t in wide[0]] for _ in range(7)]
+        wide += [distinct(wide[0], n) for n in range(1, 8)]
         torch.cuda.synchronize()
         log(f"wide layer ready in {time.time() - t0:.1f}s")
         c5 = []
