@@ -80,3 +80,14 @@ def test_source_hash_covers_every_kernel_source():
     csrc = os.path.join(bench.ROOT, "moe_gate_up_amd", "csrc")
     files = [f for f in os.listdir(csrc) if f.endswith((".hpp", ".hip"))]
     assert "moe_decode.hip" in files and "router.hpp" in files and len(files) >= 8
+
+
+@pytest.mark.parametrize("B,expect", [
+    (1, "gate_up per-slot, down per-token"),
+    (8, "gate_up per-slot, down matrix-core grouped"),
+    (32, "gate_up matrix-core grouped, down matrix-core grouped"),
+])
+def test_kernel_choice_names_the_table_s_kernels(B, expect):
+    # the names bench prints beside each timed row come from the library's own
+    # plan calls (host-only: no GPU needed), H=2048, I=768, 128 experts, top-8
+    assert bench.kernel_choice(B, 2048, 768, 128, 8) == expect
