@@ -149,10 +149,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, name: str = None, workload: dict = None):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
     reads for a copy kernel of known size) from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+    summary, if it was taken on the current kernel sources -- and, where given, on
+    the kernel `name` and the `workload` (shape and routing) asked about; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         d = json.load(open(p))
@@ -160,8 +161,12 @@ def measured_traffic(kernel: str):
         return None
     if d.get("source_hash") != kernel_source_hash():
         return None
+    if workload is not None and d.get("workload") != workload:
+        return None
     k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes")
+    if k is None or (name is not None and not k.get("template_name", "").startswith(name)):
+        return None
+    return k.get("bytes")
 
 
 def main():
@@ -541,10 +546,14 @@ def main():
                  mg.MOE_DOWN_EXPERT_GROUPED_MFMA: "moe_down_grouped_mfma_w64"}[dn_variant],
     }
 
+    # the counters in profiles/traffic.json hold for this shape and routing only
+    traffic_workload = {"B": B, "H": H, "I": I, "E": E, "k": k, "routing": "uniform"}
+
     def roofline(which):
         gbps = kern[f"{which}_GBps"]
         return {"bound": "hbm", "kernel": names[which], "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(which),
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(which, names[which], traffic_workload),
                 "algorithmic_bytes_per_launch": round(kern[f"{which}_bytes_per_launch"]),
                 "us_per_launch": round(kern[f"{which}_us"], 3)}
 

@@ -62,6 +62,29 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("gate_up") is None
 
 
+def test_traffic_reported_only_for_its_kernel_and_workload(tmp_path, monkeypatch):
+    """The counters were taken on one kernel at one workload: another batch size,
+    shape or routing, or the table's other kernel at that size, gets None."""
+    h = bench.kernel_source_hash()
+    wl = {"B": 32, "H": 2048, "I": 768, "E": 128, "k": 8, "routing": "uniform"}
+    data = {"source_hash": h, "workload": wl,
+            "kernels": {"gate_up": {"template_name": "moe_gate_up_grouped_mfma_w64", "bytes": 123}}}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(data))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
+    assert bench.measured_traffic("gate_up", "moe_gate_up_grouped_mfma_w64", dict(wl)) == 123
+    assert bench.measured_traffic("gate_up", "moe_gate_up_3d_batched_w64", dict(wl)) is None
+    assert bench.measured_traffic("gate_up", "moe_gate_up_grouped_mfma_w64", dict(wl, B=1)) is None
+    assert bench.measured_traffic("gate_up", "moe_gate_up_grouped_mfma_w64", dict(wl, routing="zipf")) is None
+
+
+def test_committed_traffic_names_its_workload():
+    d = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic.json")))
+    assert d["workload"] == {"B": 32, "H": 2048, "I": 768, "E": 128, "k": 8, "routing": "uniform"}
+    assert set(d["kernels"]) == {"gate_up", "down"}
+
+
 def test_source_hash_covers_the_build_flags(tmp_path, monkeypatch):
     """A change of the compiler flags changes the hash (and so voids stored counters)."""
     h = bench.kernel_source_hash()
