@@ -153,7 +153,9 @@ int moe_decode_down(const void *h, const int32_t *topk_ids, const float *topk_we
  *     (rows_per_wave must be 0 or 8).
  * The plain call takes the matrix-core grouped variant once 16*B*k >= 5E
  * (5/16 of a slot per expert on average) and its limits allow it, else the
- * per-token one: the fastest in each measured configuration.  The vector-unit
+ * per-token one: the fastest in each measured configuration but one (H =
+ * 4096 with 5 tokens of uniform routing, where the per-token kernel is 3.5 %
+ * faster; under skewed routing it is 6 % slower there).  The vector-unit
  * grouped variant runs on request only: its limits lie within the
  * matrix-core one's, which is faster wherever both run. */
 #define MOE_DOWN_PER_TOKEN 1

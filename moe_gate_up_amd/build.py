@@ -7,15 +7,23 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "moe_decode.hip")
 OUT = os.path.join(HERE, "libmoe_decode.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+
+# Translation units and their own flags.  The two down kernel families take
+# other instruction-scheduling strategies than the rest of the library (why,
+# with the measurements, in csrc/host.hpp).
+SOURCES = [
+    ("moe_decode.hip", []),
+    ("down_token.hip", ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]),
+    ("down_mfma.hip", ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # kernel arguments preloaded into SGPRs when the wave starts: one scalar
@@ -33,16 +41,35 @@ def hipcc() -> str:
     return "hipcc"
 
 
+def _run(cmds, verbose):
+    """Run the commands in parallel; raise with the first failure's messages."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = None
+    for p in procs:
+        _, stderr = p.communicate()
+        err = "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+        if p.returncode != 0 and failed is None:
+            failed = f"hipcc failed ({p.returncode}):\n{err}"
+        elif err and verbose:
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError(failed)
+
+
 def build(out: str = OUT, verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), SRC, "-o", out + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if err and verbose:
-        print(err, file=sys.stderr)
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    objs, cmds = [], []
+    for src, extra in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *HIPCC_FLAGS, *extra, *inc, "-c", os.path.join(HERE, "csrc", src), "-o", obj])
+    _run(cmds, verbose)
+    _run([[hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", out + ".tmp"]], verbose)
     os.replace(out + ".tmp", out)
     return out
 

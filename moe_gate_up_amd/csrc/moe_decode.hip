@@ -7,21 +7,25 @@
 #include <utility>
 
 #include "moe_decode.h"
-#include "down.hpp"
 #include "down_grouped.hpp"
-#include "down_grouped_mfma.hpp"
+#include "down_grouped_mfma.hpp"   // the matrix-core down kernel's limits (the kernel itself: down_mfma.hip)
 #include "conventional.hpp"
 #include "gate_up.hpp"
 #include "gate_up_grouped.hpp"
 #include "gate_up_grouped_mfma.hpp"
 #include "peak.hpp"
+#include "host.hpp"
 #include "router.hpp"
 
 namespace {
 
-constexpr int kWavesPerBlock = 4;   // 256 threads = 4 independent 64-lane wavefronts
+using moe_host::DownLaunch;
+using moe_host::kLdsPerCu;
+using moe_host::kMaxDevices;
+using moe_host::kMaxDownPasses;
+using moe_host::kWavesPerBlock;
+using moe_host::PerDeviceOnce;
 constexpr int kMaxGateUpPasses = 8;   // H <= 8 passes of 1024 elements = 8192
-constexpr int kMaxDownPasses = 16;    // k * I <= 16 passes of 1024 elements = 16384
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -262,7 +266,6 @@ GateUpLaunch pick_grouped(int nch, int r) {
 // tokens: 74.7 vs 75.8 us, Zipf 71.5 vs 77.1: an expert shared by more
 // tokens is cut into fewer units, each of which reads its rows).
 constexpr long long kMfmaCus = 256;
-constexpr int kLdsPerCu = 160 * 1024;
 // LDS the residency count is computed against: three workgroups of 54,272
 // bytes each (162,816 in all) did not fit one CU on MI355X, three of 53,760 did
 constexpr int kLdsPerCuUsable = kLdsPerCu - 2048;
@@ -290,24 +293,6 @@ bool mfma_allowed(int H, long long slots, int E) {
 // Occupancy follows the LDS size each launch asks for, not this maximum.
 constexpr int kMfmaMaxLds = moe::mfma_lds_bytes(moe::kSortMaxExperts, moe::kSortMaxSlots, 8192, moe::kMfmaColumns);
 static_assert(kMfmaMaxLds <= kLdsPerCu, "the matrix-core kernel's largest LDS must fit one CU");
-
-constexpr int kMaxDevices = 64;
-
-// Runs f() once per device, on the first call made with that device current,
-// and returns its result on every call.
-struct PerDeviceOnce {
-  std::once_flag flag[kMaxDevices];
-  hipError_t rc[kMaxDevices];
-  template <class F>
-  hipError_t operator()(F f) {
-    int dev = 0;
-    hipError_t r = hipGetDevice(&dev);
-    if (r != hipSuccess) return r;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::call_once(flag[dev], [&] { rc[dev] = f(); });
-    return rc[dev];
-  }
-};
 
 PerDeviceOnce g_gate_up_mfma_setup;
 
@@ -470,10 +455,8 @@ int gate_up_impl(const void* x, const int32_t* ids, const uint8_t* wg, const uin
 }
 
 // ---------------------------------------------------------------- down
-// register budget per pass: R weight chunks (4 VGPRs) + R scales + h (8 VGPRs)
-constexpr bool down_fits(int np, int r) { return np * (5 * r + 8) <= 224; }
 bool down_allowed(int np, int r) {
-  return (r == 1 || r == 2 || r == 4 || r == 8) && np >= 1 && np <= kMaxDownPasses && down_fits(np, r);
+  return (r == 1 || r == 2 || r == 4 || r == 8) && np >= 1 && np <= kMaxDownPasses && moe_host::down_fits(np, r);
 }
 
 // The down wave streams k rows per output, so far fewer wavefronts suffice:
@@ -486,52 +469,9 @@ int down_default_rows(int B, int H, int I, int k) {
 }
 
 // Down launchers, like the gate/up ones, return their number of workgroups
-// and launch only when `go` is set.
-//
-// Per-token grid: one wavefront per (tile of R outputs, token), 4 tiles of one
-// token per workgroup; dynamic LDS: h[b] of the workgroup's token, 2*k*I <= 32 KB.
-template <int NP, int R>
-long long launch_down_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
-                        const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
-  const int tiles = (H + R - 1) / R;
-  const long long blocks = ((long long)tiles * B + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (!go) return blocks;
-  hipLaunchKernelGGL((moe::moe_down_3d_batched_w64<NP, R>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
-                     (unsigned)(2 * k * I), st, static_cast<const uint16_t*>(h), ids, tw, wd, sd,
-                     static_cast<uint16_t*>(y), B, H, I, E, k, tiles);
-  return blocks;
-}
-
-using DownLaunch = long long (*)(bool, hipStream_t, const void*, const int32_t*, const float*, const uint8_t*,
-                                 const uint8_t*, void*, int, int, int, int, int);
-
-template <int NP, int R>
-DownLaunch down_fn() {
-  if constexpr (down_fits(NP, R)) return launch_down_t<NP, R>;
-  else return nullptr;
-}
-
-template <int NP>
-DownLaunch pick_down_r(int r) {
-  switch (r) {
-    case 1: return down_fn<NP, 1>();
-    case 2: return down_fn<NP, 2>();
-    case 4: return down_fn<NP, 4>();
-    case 8: return down_fn<NP, 8>();
-  }
-  return nullptr;
-}
-
-template <int... NPs>
-DownLaunch pick_down_np(int np, int r, std::integer_sequence<int, NPs...>) {
-  DownLaunch fn = nullptr;
-  ((np == NPs + 1 ? (fn = pick_down_r<NPs + 1>(r), 0) : 0), ...);
-  return fn;
-}
-
-DownLaunch pick_down(int np, int r) {
-  return pick_down_np(np, r, std::make_integer_sequence<int, kMaxDownPasses>{});
-}
+// and launch only when `go` is set (moe_host::DownLaunch).  The per-token and
+// the matrix-core kernels are launched from their own translation units
+// (down_token.hip, down_mfma.hip); the vector-unit grouped one from here.
 
 // ---------------------------------------------------------------- down, expert-grouped
 // One workgroup per 8 (I <= 1024) or 4 output dimensions, at most two passes
@@ -569,66 +509,17 @@ bool down_mfma_allowed(int I, long long slots, int E) {
   return (I + 255) / 256 <= moe::kDownMfmaMaxRounds && slots <= moe::kSortMaxSlots && E <= moe::kSortMaxExperts;
 }
 
-// Largest dynamic LDS of the matrix-core down kernel with NR rounds.
-template <int NR>
-constexpr int down_mfma_max_lds() { return moe::down_mfma_lds_bytes(NR, moe::kSortMaxExperts, moe::kSortMaxSlots); }
-template <int... NRs>
-constexpr bool down_mfma_lds_fits(std::integer_sequence<int, NRs...>) {
-  return ((down_mfma_max_lds<NRs + 1>() <= kLdsPerCu) && ...);
-}
-static_assert(down_mfma_lds_fits(std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{}),
-              "the matrix-core down kernel's largest LDS must fit one CU");
-
-// Each instantiation's maximum dynamic LDS is set once per device (the
-// largest its limits allow), like the matrix-core gate/up kernel's.
-template <int... NRs>
-hipError_t down_mfma_set_lds(std::integer_sequence<int, NRs...>) {
-  hipError_t rc = hipSuccess;
-  ((rc = rc != hipSuccess ? rc
-                          : hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::moe_down_grouped_mfma_w64<NRs + 1>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                down_mfma_max_lds<NRs + 1>())),
-   ...);
-  return rc;
-}
-
-PerDeviceOnce g_down_mfma_setup;
-hipError_t down_mfma_setup_current_device() {
-  return g_down_mfma_setup(
-      [] { return down_mfma_set_lds(std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{}); });
-}
-
-template <int NR>
-long long launch_down_mfma_t(bool go, hipStream_t st, const void* h, const int32_t* ids, const float* tw,
-                             const uint8_t* wd, const uint8_t* sd, void* y, int B, int H, int I, int E, int k) {
-  const long long blocks = H / moe::kDownMfmaRows;   // H is a multiple of 32
-  if (!go) return blocks;
-  hipLaunchKernelGGL((moe::moe_down_grouped_mfma_w64<NR>), dim3((unsigned)blocks), dim3(64 * moe::down_mfma_waves(NR)),
-                     (unsigned)moe::down_mfma_lds_bytes(NR, E, B * k), st, static_cast<const uint16_t*>(h), ids, tw, wd, sd,
-                     static_cast<uint16_t*>(y), B, H, I, E, k);
-  return blocks;
-}
-
-template <int... NRs>
-DownLaunch pick_down_mfma_nr(int nr, std::integer_sequence<int, NRs...>) {
-  DownLaunch fn = nullptr;
-  ((nr == NRs + 1 ? (fn = launch_down_mfma_t<NRs + 1>, 0) : 0), ...);
-  return fn;
-}
-
-DownLaunch pick_down_mfma(int I) {
-  return pick_down_mfma_nr((I + 255) / 256, std::make_integer_sequence<int, moe::kDownMfmaMaxRounds>{});
-}
-
 // Variant table (graph-timed sweeps of the down kernel alone on MI355X, 128
 // experts, top-8, uniform routing unless stated): the per-token kernel while
 // few tokens share an expert, the matrix-core grouped one from 5/16 of a slot
-// per expert on (H = 2048, I = 768: 4 tokens 11.0 per-token vs 11.5 us, 5
-// tokens 13.4 vs 13.0, 6 tokens 14.4 vs 14.4, 8 tokens 17.8 vs 16.7, 16
-// tokens 30.3 vs 24.1; H = 4096, I = 1536: 4 tokens 36.2 vs 38.5, 5 tokens
-// 44.0 vs 44.0, 6 tokens 51.8 vs 49.5, 8 tokens 66.2 vs 57.8).  Skewed
-// routing favours the grouped kernels earlier (H = 4096, 4 tokens, Zipf: 33.0
-// per-token, 31.8 on the matrix cores).  The vector-unit grouped kernel is
+// per expert on (H = 2048, I = 768: 4 tokens 10.4 per-token vs 11.4 us, 5
+// tokens 13.1 vs 12.9, 6 tokens 14.0 vs 14.2; H = 4096, I = 1536: 4 tokens
+// 34.8 vs 38.2, 5 tokens 42.1 vs 43.7, 6 tokens 49.5 vs 49.2, 7 tokens 56.9
+// vs 54.7, 8 tokens 62.9 vs 57.4).  Skewed routing favours the grouped
+// kernels earlier (Zipf: H = 2048, 6 tokens 12.2 per-token vs 11.7; H =
+// 4096, 5 tokens 37.7 vs 35.6, 6 tokens 43.9 vs 39.0), so the one threshold
+// stays where uniform routing at H = 2048 puts it, although uniform routing
+// at H = 4096 alone would move it to 6 tokens.  The vector-unit grouped kernel is
 // never the table's choice: every shape it takes, the matrix-core kernel
 // takes too, faster (per-token against it: H = 2048, 8 tokens 17.8 vs 17.3,
 // 16 tokens 30.3 vs 25.3; H = 4096, 8 tokens 66.1 vs 62.8); it runs on
@@ -648,7 +539,7 @@ DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, in
   if (variant == MOE_DOWN_PER_TOKEN) {
     const int np = passes((long long)k * I);
     if (rows == 0) rows = down_default_rows(B, H, I, k);
-    return down_allowed(np, rows) ? pick_down(np, rows) : nullptr;
+    return down_allowed(np, rows) ? moe_host::pick_down(np, rows) : nullptr;
   }
   if (variant == MOE_DOWN_EXPERT_GROUPED) {
     const int ro = moe::down_grouped_rows(passes(I));
@@ -659,7 +550,7 @@ DownLaunch down_launcher(int& variant, int& rows, int B, int H, int I, int E, in
   if (variant == MOE_DOWN_EXPERT_GROUPED_MFMA) {
     if (rows == 0) rows = moe::kDownMfmaRows;
     if (rows != moe::kDownMfmaRows || !down_mfma_allowed(I, (long long)B * k, E)) return nullptr;
-    return pick_down_mfma(I);
+    return moe_host::pick_down_mfma(I);
   }
   return nullptr;
 }
@@ -678,7 +569,8 @@ int down_impl(const void* h, const int32_t* ids, const float* tw, const uint8_t*
     return MOE_ERR_ALIAS;
   DownLaunch fn = down_launcher(variant, rows, B, H, I, E, k);
   if (!fn) return MOE_ERR_ARG;
-  if (variant == MOE_DOWN_EXPERT_GROUPED_MFMA && down_mfma_setup_current_device() != hipSuccess) return MOE_ERR_LAUNCH;
+  if (variant == MOE_DOWN_EXPERT_GROUPED_MFMA && moe_host::down_mfma_setup_current_device() != hipSuccess)
+    return MOE_ERR_LAUNCH;
   (void)hipGetLastError();
   fn(true, static_cast<hipStream_t>(stream), h, ids, tw, wd, sd, y, B, H, I, E, k);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;

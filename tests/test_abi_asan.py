@@ -1,7 +1,8 @@
 """The C ABI's host code under AddressSanitizer (CPU only).
 
-The library is built with the sanitizer on its host code only (the device
-code is compiled as usual, without it), and a small C++ program
+The library (every translation unit of it) is built with the sanitizer on its
+host code only (the device code is compiled as usual, without it; the per-unit
+scheduling flags do not matter here), and a small C++ program
 (`abi_host_asan.cpp`, built with the same compiler and sanitizer runtime)
 drives every entry point's argument validation and the built-in table over a
 grid of shapes.  No call reaches a launch, so no GPU is needed; a sanitizer
@@ -12,6 +13,8 @@ import shutil
 import subprocess
 
 import pytest
+
+from moe_gate_up_amd.build import SOURCES   # every translation unit of the library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -28,7 +31,7 @@ def test_host_code_under_address_sanitizer(tmp_path):
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                     "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", *inc,
-                    os.path.join(ROOT, "moe_gate_up_amd", "csrc", "moe_decode.hip"), "-o", str(lib)],
+                    *[os.path.join(ROOT, "moe_gate_up_amd", "csrc", src) for src, _ in SOURCES], "-o", str(lib)],
                    check=True, capture_output=True, timeout=600)
     subprocess.run([CLANG, "-O1", "-g", "-std=c++17", "-fsanitize=address", "-fno-omit-frame-pointer",
                     "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_host_asan.cpp"),
